@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs shared by the oracle side and the GPU side.
+
+``allocator.BlockAllocator`` builds block tables, slot mappings and CoW pairs;
+``configs.make_config(i)`` builds the five decode-step workloads. No attention
+arithmetic lives here.
+"""
+
+from .allocator import BlockAllocator  # noqa: F401
+from .configs import BLOCK_SIZE, CONFIG_NAMES, Workload, make_config, poison_unused  # noqa: F401
