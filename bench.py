@@ -1,0 +1,245 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step = the whole hot path over one batch: copy_blocks (CoW pairs, if the
+workload has any) -> reshape_and_cache (each sequence's new token) ->
+paged_attention_decode (partition launch + merge launch). The default workload
+is the LLaMA-7B-shape decode batch: 64 sequences, 32 heads x 128, fp16, block
+size 16, context lengths uniform in [128, 2048].
+
+Inputs are resident in HBM before timing starts. The pools are replicated R
+times at different addresses and the steps rotate through the replicas, so no
+step finds the previous step's K/V in the 256 MB last-level cache.
+
+Printed: one JSON line with the step throughput (algorithmic K+V bytes per
+second), the decode kernel's roofline fraction from HIP events recorded around
+every partition launch inside the timed region, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
+METRIC = "paged decode attention KV GB/s + seqs/s, % of MI355X HBM peak (LLaMA-7B shape)"
+DECODE_SOURCES = ["paged_kv_cache_159_amd/csrc/pkv_decode.hip",
+                  "paged_kv_cache_159_amd/csrc/pkv_device.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, help="workload index 1..5 (default 2)")
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU work budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move, per launch, stated per unit:
+    decode: K+V of every valid token (num_heads*head_dim*2 B each for K and V:
+    16 KiB per token at 32 x 128 fp16), the query and output rows, the block
+    table entries of the valid blocks and the context lengths;
+    write: each new token's K+V read once and written once, plus its slot;
+    copy: each CoW block read once and written once, K and V."""
+    kvt = w.kv_bytes_per_token
+    rowb = w.num_heads * w.head_dim * 2
+    nblocks = int(((w.context_lens.astype(np.int64) + w.block_size - 1) // w.block_size).sum())
+    decode = w.total_context * kvt + 2 * w.num_seqs * rowb + 4 * nblocks + 4 * w.num_seqs
+    T = len(w.slot_mapping)
+    write = 2 * T * kvt + 8 * T
+    copy = len(w.copy_pairs) * (2 * 2 * w.block_size * rowb + 8)
+    return decode, write, copy
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM traffic per decode launch from committed rocprofv3 counter runs,
+    only if they were taken on the current decode kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("decode_source_digest") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle (as it is) on whole sequences of the same workload,
+    one thread, until about budget_s seconds of CPU work; scaled to K+V GB/s."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    t0 = time.perf_counter()
+    done_tokens = 0
+    done_seqs = 0
+    K, V = w.key_cache, w.value_cache
+    if len(w.copy_pairs):
+        K, V = oracle.copy_blocks(K, V, w.copy_pairs)
+    K, V = oracle.reshape_and_cache(w.new_key, w.new_value, K, V, w.slot_mapping, w.block_size)
+    t_prep = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s in range(w.num_seqs):
+            pairs = [(s, h) for h in range(w.num_heads)]
+            oracle.paged_attention_decode(w.query, K, V, w.block_tables, w.context_lens, w.scale,
+                                          w.block_size, w.dtype, pairs=pairs)
+            done_tokens += int(w.context_lens[s])
+            done_seqs += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    gbs = done_tokens * w.kv_bytes_per_token / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle, one thread, first {done_seqs} of {w.num_seqs} sequences "
+                      f"(all {w.num_heads} heads, {done_tokens} tokens) in {el:.1f} s; "
+                      f"host cache write/copy prep {t_prep:.1f} s not counted",
+            "seqs_per_s": round(done_seqs / el, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_159_amd as pkv
+    from workloads import make_config
+    from workloads.device import upload
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    pkv.lib()
+
+    t0 = time.time()
+    w = make_config(args.workload)
+    print(f"[bench] workload {w.index} {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} "
+          f"{w.dtype} NB={w.num_blocks} sum(ctx)={w.total_context} generated in {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    dw = upload(w, dev)
+    pool_bytes = 2 * dw.key_cache.numel() * 2
+    R = args.replicas or max(2, int(np.ceil(4.0e9 / pool_bytes)))
+    R = min(R, 16)
+    kcs = [dw.key_cache] + [dw.key_cache.clone() for _ in range(R - 1)]
+    vcs = [dw.value_cache] + [dw.value_cache.clone() for _ in range(R - 1)]
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq, device=dev)
+    outs = [torch.empty_like(dw.query) for _ in range(R)]
+    dec_b, write_b, copy_b = algorithmic_bytes(w)
+    step_bytes = dec_b + write_b + copy_b
+    has_copy = len(w.copy_pairs) > 0
+    print(f"[bench] {R} pool replicas of {pool_bytes / 1e9:.2f} GB; algorithmic bytes/step: "
+          f"decode {dec_b} write {write_b} copy {copy_b}", file=sys.stderr, flush=True)
+
+    ev = []
+
+    def step(i, record):
+        r = i % R
+        kc, vc = kcs[r], vcs[r]
+        if has_copy:
+            pkv.copy_blocks(kc, vc, dw.copy_pairs)
+        pkv.reshape_and_cache(dw.new_key, dw.new_value, kc, vc, dw.slot_mapping)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        pkv.paged_attention_decode_partitions(outs[r], dw.query, kc, vc, dw.block_tables,
+                                              dw.context_lens, w.scale, ws)
+        if record:
+            e1.record()
+            ev.append((e0, e1))
+        pkv.paged_attention_decode_merge(outs[r], dw.context_lens, w.max_blocks_per_seq, ws)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = wall / args.steps * 1e3
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    dec_avg_us = float(np.mean(dec_us))
+    achieved = dec_b / (dec_avg_us * 1e-6) / 1e9
+    value = step_bytes / (ms * 1e-3) / 1e9
+    print(f"[bench] {ms * 1e3:.1f} us/step; partition kernel avg {dec_avg_us:.1f} us "
+          f"(p10 {np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f}) -> "
+          f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak", file=sys.stderr, flush=True)
+
+    traffic = load_traffic(w.name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded shuffled block tables)",
+        "config": {
+            "workload": f"{w.name}: {w.num_seqs} seqs x {w.num_heads} heads x {w.head_dim}, {w.dtype} KV, "
+                        f"block_size {w.block_size}, sum(ctx)={w.total_context}, "
+                        f"{len(w.slot_mapping)} new tokens, {len(w.copy_pairs)} CoW pairs",
+            "global_batch": w.num_seqs,
+            "max_context": int(w.context_lens.max()),
+            "parallelism": "single GPU",
+        },
+        "seqs_per_s": round(w.num_seqs / (ms * 1e-3), 1),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "decode_partition_us": round(dec_avg_us, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_partition_kernel",
+            "bytes_per_launch": dec_b,
+        },
+    }
+    del kcs, vcs
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

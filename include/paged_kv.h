@@ -1,0 +1,170 @@
+/*
+ * paged_kv.h — C ABI of libpaged_kv.so: paged KV-cache decode attention, the
+ * slot-mapped cache write and the copy-on-write block copy, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [P1] "3.3 页面级显存管理" (page-level GPU memory management), aiknowledge.cn/article/68056
+ *   [P2] "vLLM三大核心技术分页内存与共享解码", aiqz.cc/article/vllm-core-techniques.html
+ *   [P3] "3.1 PagedAttention的核心原理", aiknowledge.cn/article/68054
+ *   [P4] reading notes on "vLLM: Easy, Fast, and Cheap LLM Serving with PagedAttention",
+ *        zmoe.com/3008.html
+ *
+ * Common conventions
+ * ------------------
+ * Element types: PKV_F16 (IEEE binary16) or PKV_BF16 (bfloat16). Every 16-bit
+ * tensor of one call has the same type.
+ *
+ * Layouts (all row-major and dense; every pointer 16-byte aligned):
+ *   key_cache, value_cache  [num_blocks][block_size][num_heads][head_dim]
+ *       One physical block ("page") holds block_size consecutive tokens; one
+ *       token holds num_heads*head_dim elements (kv_dim). The element of token
+ *       t of a sequence is at physical*block_size*kv_dim + (t % block_size)*kv_dim
+ *       with physical = block_table[t / block_size] [P3 §3.1.3 "逻辑地址到物理地址
+ *       的转换"; P3 §3.1.2 "页面结构设计" gives separate Key and Value caches].
+ *   query, out              [num_seqs][num_heads][head_dim]
+ *   block_tables            int32 [num_seqs][max_blocks_per_seq], one flattened
+ *       table per sequence [P3 §3.1.3: a flat block_table array]; entries at
+ *       and past ceil(context_len / block_size) are never read.
+ *   context_lens            int32 [num_seqs]
+ *   slot_mapping            int64 [num_tokens]; slot = physical*block_size + offset
+ *   block_mapping           int32 [num_pairs][2] = (src, dst)
+ *
+ * Supported now: block_size 16 (the pages' default: P2 "KV Cache逻辑块物理块映射
+ * 机制"; P4 "块大小"), head_dim 64 or 128, any num_heads >= 1.
+ *
+ * Ownership: the caller owns every buffer (pools, query, out, tables,
+ * workspace). The library allocates and frees nothing and keeps no state
+ * between calls. All pointers except `stream` are device pointers.
+ *
+ * Execution: every call validates its scalar arguments and pointers on the
+ * host, then enqueues kernels on `stream` (a hipStream_t; NULL is the default
+ * stream) and returns without synchronising. A launch failure reported by
+ * hipGetLastError becomes PKV_ERR_LAUNCH. Nothing is thrown across the ABI.
+ *
+ * Data-dependent preconditions are the caller's (checking them would need a
+ * device synchronisation): block-table entries that are read lie in
+ * [0, num_blocks); 1 <= context_lens[s] <= max_blocks_per_seq*block_size;
+ * slots are < num_blocks*block_size and unique within a call; copy pairs have
+ * unique destinations that are not sources in the same call.
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* a count is out of range or sizes overflow */
+  PKV_ERR_UNSUPPORTED = -3, /* dtype, block_size or head_dim not supported */
+  PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  PKV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_ALIGN = -6        /* a pointer is not 16-byte aligned */
+} pkv_status;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* pkv_status_string(int status);
+
+/*
+ * Workspace bytes paged_attention_decode needs for these sizes: fp32 partial
+ * results (running max, exponent sum and a head_dim vector) of every
+ * 512-token context partition of every (sequence, head). Returns 0 when no
+ * sequence can span more than one partition (max_blocks_per_seq*block_size
+ * <= 512) or when the arguments are invalid.
+ */
+size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                      int max_blocks_per_seq, int block_size);
+
+/*
+ * Single-query decode attention over the paged cache [P3 §3.1.3 translation;
+ * P1 §3.3.1 "显存访问模式的优化": work organised by physical block, all
+ * sequences in one launch]. For every sequence s and head h:
+ *     x_t = scale * <query[s][h], K_t>  for tokens t in [0, context_lens[s])
+ *     out[s][h] = sum_t softmax(x)_t * V_t
+ * where K_t and V_t are token t's rows of head h, found through block_tables[s].
+ * Accumulation is fp32; the output is rounded to nearest-even into `dtype`.
+ * Contexts longer than 512 tokens are split into 512-token partitions whose
+ * partial results are merged by log-sum-exp; the reduction order depends only
+ * on logical token positions, so relabelling physical blocks leaves `out`
+ * bit-identical.
+ * `workspace` (>= paged_attention_workspace_size(...) bytes, any content) may
+ * be NULL when that size is 0. num_seqs == 0 is a no-op (pointers may then be
+ * NULL).
+ * Equivalent to paged_attention_decode_partitions followed by
+ * paged_attention_decode_merge on the same stream.
+ */
+int paged_attention_decode(void* out, const void* query,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int num_heads, int head_dim, int num_blocks,
+                           int block_size, int max_blocks_per_seq, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * First of the two launches of paged_attention_decode: one workgroup per
+ * (sequence, head, 512-token partition). Sequences whose context fits one
+ * partition get their final `out` here; the others leave partials in
+ * `workspace`. Exposed so that callers can schedule or time the two launches
+ * separately; the arguments mean the same as for paged_attention_decode.
+ */
+int paged_attention_decode_partitions(void* out, const void* query,
+                                      const void* key_cache, const void* value_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int num_seqs, int num_heads, int head_dim, int num_blocks,
+                                      int block_size, int max_blocks_per_seq, float scale,
+                                      int dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
+ * Second launch: log-sum-exp merge of the partials left by
+ * paged_attention_decode_partitions for sequences longer than one partition,
+ * writing their `out`. Must follow that call on the same stream, with the
+ * same out, context_lens, sizes and workspace. Does nothing (and launches
+ * nothing) when max_blocks_per_seq*block_size <= 512.
+ */
+int paged_attention_decode_merge(void* out, const int32_t* context_lens,
+                                 int num_seqs, int num_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Slot-mapped cache write [P2 "Copy-on-Write共享解码的显存优化原理": the new
+ * token's K/V is written into its block; P1 §3.3.2 "动态页面分配机制"]. For each
+ * token i with slot_mapping[i] >= 0:
+ *     key_cache[slot / block_size][slot % block_size] = key[i]   ([num_heads][head_dim])
+ *     value_cache[...]                                 = value[i]
+ * A negative slot marks a padding token and is skipped. key and value are
+ * [num_tokens][num_heads][head_dim]. The copy is bit-exact. num_tokens == 0 is
+ * a no-op (pointers may then be NULL).
+ */
+int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_heads, int head_dim,
+                      int num_blocks, int block_size, int dtype, void* stream);
+
+/*
+ * Copy-on-write block copy [P2 "Python 演示" copy_on_write: the caller copies
+ * the data into the newly allocated block; P3 §3.1.5 "CoW机制的实现" step 3;
+ * P4 "Memory Sharing与写时复制"]. For each pair (src, dst) in block_mapping,
+ * the whole block dst of both pools becomes a bit-exact copy of block src.
+ * num_pairs == 0 is a no-op (pointers may then be NULL).
+ */
+int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping, int num_pairs,
+                int num_heads, int head_dim, int num_blocks, int block_size, int dtype,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

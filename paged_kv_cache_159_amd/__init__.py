@@ -1,0 +1,18 @@
+"""MI355X-native paged KV-cache decode attention.
+
+The product is libpaged_kv.so (hand-written gfx950 HIP kernels behind the C
+ABI in include/paged_kv.h); this package is its thin torch binding. Importing
+the package does not load the library; the first call does, and fails loudly
+if it is not built.
+"""
+
+from ._lib import PagedKVError, lib  # noqa: F401
+from .ops import (  # noqa: F401
+    alloc_workspace,
+    copy_blocks,
+    paged_attention_decode,
+    paged_attention_decode_merge,
+    paged_attention_decode_partitions,
+    reshape_and_cache,
+    workspace_size,
+)

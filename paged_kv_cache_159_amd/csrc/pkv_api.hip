@@ -1,0 +1,217 @@
+// C ABI of libpaged_kv.so (declared in include/paged_kv.h): host-side argument
+// validation, workspace sizing and dispatch to the gfx950 launchers. Nothing
+// here allocates, synchronises or keeps state; every check runs before the
+// first HIP call, so invalid arguments never reach the device.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "paged_kv.h"
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Checks common to every call: element type, block size, head geometry, pool.
+int check_layout(int dtype, int block_size, int num_heads, int head_dim, int num_blocks) {
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (block_size != pkv::kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (num_heads < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
+  // in-block element offsets are 32-bit
+  if ((int64_t)num_heads * head_dim * block_size > kMaxGrid) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+int num_partitions(int max_blocks_per_seq, int block_size) {
+  const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
+  return (int)((tokens + pkv::kPartitionTokens - 1) / pkv::kPartitionTokens);
+}
+
+// Validation shared by the decode entry points. Fills *parts and *need.
+int check_decode(int num_seqs, int num_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int* parts, size_t* need) {
+  if (num_seqs < 0 || max_blocks_per_seq < 1) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxGrid) return PKV_ERR_SHAPE;
+  *parts = num_partitions(max_blocks_per_seq, block_size);
+  if ((int64_t)num_seqs * num_heads * (*parts) > kMaxGrid) return PKV_ERR_SHAPE;
+  *need = (*parts > 1) ? pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, *parts) : 0;
+  return PKV_OK;
+}
+
+int check_workspace(void* ws, size_t bytes, size_t need) {
+  if (need == 0) return PKV_OK;
+  if (ws == nullptr || bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return PKV_ERR_ALIGN;
+  return PKV_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void* key_cache,
+                   const void* value_cache, const int32_t* block_tables,
+                   const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
+                   int num_blocks, int block_size, int max_blocks_per_seq, float scale, int dtype,
+                   void* workspace, size_t workspace_bytes) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, num_blocks);
+  if (rc) return rc;
+  int parts = 0;
+  size_t need = 0;
+  rc = check_decode(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, &parts, &need);
+  if (rc) return rc;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;  // nothing to do; empty tensors may carry NULL
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens))
+    return PKV_ERR_ALIGN;
+  rc = check_workspace(workspace, workspace_bytes, need);
+  if (rc) return rc;
+  a->out = out;
+  a->query = query;
+  a->key_cache = key_cache;
+  a->value_cache = value_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->num_seqs = num_seqs;
+  a->num_heads = num_heads;
+  a->head_dim = head_dim;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->num_parts = parts;
+  a->scale = scale;
+  a->dtype = dtype;
+  a->ws_ml = nullptr;
+  a->ws_o = nullptr;
+  if (need) pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a->ws_ml, &a->ws_o);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return kVersion; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "success";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "argument out of range (count, size overflow or non-finite scale)";
+    case PKV_ERR_UNSUPPORTED: return "unsupported dtype, block_size or head_dim";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                      int max_blocks_per_seq, int block_size) {
+  if (check_layout(PKV_F16, block_size, num_heads, head_dim, 1)) return 0;
+  int parts = 0;
+  size_t need = 0;
+  if (check_decode(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, &parts, &need))
+    return 0;
+  return need;
+}
+
+int paged_attention_decode_partitions(void* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int num_seqs, int num_heads,
+                                      int head_dim, int num_blocks, int block_size,
+                                      int max_blocks_per_seq, float scale, int dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::DecodeArgs a;
+  int rc = prepare_decode(&a, out, query, key_cache, value_cache, block_tables, context_lens,
+                          num_seqs, num_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq, scale, dtype, workspace, workspace_bytes);
+  if (rc || num_seqs == 0) return rc;
+  return status_of(pkv::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
+}
+
+int paged_attention_decode_merge(void* out, const int32_t* context_lens, int num_seqs,
+                                 int num_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, 1);
+  if (rc) return rc;
+  int parts = 0;
+  size_t need = 0;
+  rc = check_decode(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, &parts, &need);
+  if (rc) return rc;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !context_lens) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned4(context_lens)) return PKV_ERR_ALIGN;
+  rc = check_workspace(workspace, workspace_bytes, need);
+  if (rc) return rc;
+  if (parts <= 1) return PKV_OK;  // every sequence was finished by the first launch
+  pkv::DecodeArgs a = {};
+  a.out = out;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_parts = parts;
+  a.dtype = dtype;
+  pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a.ws_ml, &a.ws_o);
+  return status_of(pkv::launch_decode_merge(a, static_cast<hipStream_t>(stream)));
+}
+
+int paged_attention_decode(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
+                           int num_blocks, int block_size, int max_blocks_per_seq, float scale,
+                           int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::DecodeArgs a;
+  int rc = prepare_decode(&a, out, query, key_cache, value_cache, block_tables, context_lens,
+                          num_seqs, num_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq, scale, dtype, workspace, workspace_bytes);
+  if (rc || num_seqs == 0) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = status_of(pkv::launch_decode_partitions(a, st));
+  if (rc || a.num_parts <= 1) return rc;
+  return status_of(pkv::launch_decode_merge(a, st));
+}
+
+int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_heads, int head_dim,
+                      int num_blocks, int block_size, int dtype, void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, num_blocks);
+  if (rc) return rc;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;  // empty tensors may carry NULL
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+    return PKV_ERR_ALIGN;
+  return status_of(pkv::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+                                                 num_tokens, num_heads * head_dim,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping, int num_pairs,
+                int num_heads, int head_dim, int num_blocks, int block_size, int dtype,
+                void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, num_blocks);
+  if (rc) return rc;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  const int64_t block_elems = (int64_t)block_size * num_heads * head_dim;
+  const int64_t groups = (block_elems / 8 + pkv::kCopyVecsPerGroup - 1) / pkv::kCopyVecsPerGroup;
+  if ((int64_t)num_pairs * 2 * groups > kMaxGrid) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;  // empty tensors may carry NULL
+  if (!key_cache || !value_cache || !block_mapping) return PKV_ERR_NULL;
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(block_mapping))
+    return PKV_ERR_ALIGN;
+  return status_of(pkv::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
+                                           block_elems, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Device-side helpers shared by the gfx950 kernels: 16-bit element types,
+// packed dot products, DPP reductions inside a token row, fp32 -> 16-bit
+// rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Tokens per context partition of the decode kernels (32 blocks of 16).
+constexpr int kPartitionTokens = 512;
+constexpr int kBlockSize = 16;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+struct F16 {};
+struct BF16 {};
+
+// Element-type operations on 32-bit words holding two elements (element 2i in
+// the low half, 2i+1 in the high half: the little-endian memory order).
+template <typename T> struct Elem;
+
+template <> struct Elem<F16> {
+  // v_dot2_f32_f16: fp32 result of a.lo*b.lo + a.hi*b.hi + c.
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                  false);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(half2_t, w).x;
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(half2_t, w).y;
+  }
+  // Round to nearest even (the hardware default rounding mode).
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+};
+
+template <> struct Elem<BF16> {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                           __builtin_bit_cast(bf162_t, b), c, false);
+  }
+  // bf16 is the upper half of an fp32, so widening is a shift or a mask.
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+};
+
+// DPP lane moves within a 16-lane row (gfx9 DPP control codes).
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141, // lane i <- lane 7-i within each half row
+  kDppMirror = 0x140,     // lane i <- lane 15-i within each row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group gets
+// the same, bit-identical sum (each step adds a pair symmetrically).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x += dpp_move<kDppXor1>(x);
+  x += dpp_move<kDppXor2>(x);
+  x += dpp_move<kDppHalfMirror>(x);
+  if constexpr (N == 16) x += dpp_move<kDppMirror>(x);
+  return x;
+}
+
+// 2^x with the hardware instruction (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

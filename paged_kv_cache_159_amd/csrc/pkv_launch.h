@@ -1,0 +1,47 @@
+// Host-side launchers of the gfx950 kernels. Arguments are already validated by
+// the C ABI layer (pkv_api.hip); these only pick a kernel instance and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// copy_blocks: 16-byte vectors one workgroup copies (256 threads x 4 = 16 KiB).
+constexpr int kCopyVecsPerGroup = 1024;
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs;
+  int num_heads;
+  int head_dim;
+  int max_blocks_per_seq;
+  int num_parts;        // partitions per (sequence, head) in the workspace layout
+  float scale;
+  int dtype;            // 0 fp16, 1 bf16
+  float* ws_ml;         // [num_seqs][num_heads][num_parts][2] (running max, exp sum), log2 domain
+  float* ws_o;          // [num_seqs][num_heads][num_parts][head_dim] normalised partial outputs
+};
+
+// Workspace layout shared by the two decode launches.
+size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int num_parts);
+void decode_workspace_split(void* ws, int num_seqs, int num_heads, int num_parts, float** ml,
+                            float** o);
+
+hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                    void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                                    int row_elems, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,
+                              int num_pairs, int64_t block_elems, hipStream_t stream);
+
+}  // namespace pkv

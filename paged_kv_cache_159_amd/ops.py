@@ -1,0 +1,160 @@
+"""Python binding: torch tensors in, C ABI calls out. Argument marshalling only.
+
+Every function checks devices, dtypes, shapes and contiguity, passes raw
+device pointers and torch's current HIP stream to libpaged_kv.so, and raises
+``PagedKVError`` on a non-zero status. All computation happens in the
+library's kernels; nothing here computes on the tensors.
+
+Tensor layouts (see include/paged_kv.h):
+  query, out         [num_seqs, num_heads, head_dim]          float16 | bfloat16
+  key/value_cache    [num_blocks, block_size, num_heads, head_dim]
+  block_tables       int32 [num_seqs, max_blocks_per_seq]
+  context_lens       int32 [num_seqs]
+  key, value         [num_tokens, num_heads, head_dim]
+  slot_mapping       int64 [num_tokens]
+  block_mapping      int32 [num_pairs, 2]  (src, dst)
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import PKV_BF16, PKV_F16, check, lib
+
+_DTYPES = {torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(*ts) -> int:
+    dt = ts[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}; expected float16 or bfloat16")
+    for t in ts[1:]:
+        if t.dtype != dt:
+            raise TypeError(f"dtype mismatch: {t.dtype} vs {dt}")
+    return _DTYPES[dt]
+
+
+def _on_gpu(*ts) -> None:
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU (device 'cuda')")
+    for t in ts:
+        if t.device != dev:
+            raise ValueError(f"device mismatch: {t.device} vs {dev}")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _expect(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_blocks_per_seq: int,
+                   block_size: int = 16) -> int:
+    return int(lib().paged_attention_workspace_size(num_seqs, num_heads, head_dim,
+                                                    max_blocks_per_seq, block_size))
+
+
+def alloc_workspace(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size=16,
+                    device="cuda"):
+    n = workspace_size(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, block_size):
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
+    dt = _dtype_code(out, query, key_cache, value_cache)
+    _expect(block_tables, torch.int32, 2, "block_tables")
+    _expect(context_lens, torch.int32, 1, "context_lens")
+    if query.dim() != 3 or key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("query [S,H,D] and caches [NB,bs,H,D] expected")
+    S, H, D = query.shape
+    NB, bs, H2, D2 = key_cache.shape
+    if out.shape != query.shape or (H2, D2) != (H, D) or bs != block_size:
+        raise ValueError("out/query/cache shapes disagree")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    return dt, S, H, D, NB, block_tables.shape[1]
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens,
+                           scale: float, block_size: int = 16, workspace=None) -> torch.Tensor:
+    """Decode attention into ``out`` (both launches). Returns ``out``."""
+    dt, S, H, D, NB, MB = _decode_args(out, query, key_cache, value_cache, block_tables,
+                                       context_lens, block_size)
+    if workspace is None:
+        workspace = alloc_workspace(S, H, D, MB, block_size, out.device)
+    rc = lib().paged_attention_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                                      value_cache.data_ptr(), block_tables.data_ptr(),
+                                      context_lens.data_ptr(), S, H, D, NB, block_size, MB,
+                                      float(scale), dt, workspace.data_ptr(), workspace.numel(),
+                                      _stream(out))
+    check("paged_attention_decode", rc)
+    return out
+
+
+def paged_attention_decode_partitions(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, scale: float, workspace,
+                                      block_size: int = 16) -> None:
+    dt, S, H, D, NB, MB = _decode_args(out, query, key_cache, value_cache, block_tables,
+                                       context_lens, block_size)
+    rc = lib().paged_attention_decode_partitions(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), S, H, D, NB, block_size, MB,
+        float(scale), dt, workspace.data_ptr(), workspace.numel(), _stream(out))
+    check("paged_attention_decode_partitions", rc)
+
+
+def paged_attention_decode_merge(out, context_lens, max_blocks_per_seq: int, workspace,
+                                 block_size: int = 16) -> None:
+    _on_gpu(out, context_lens, workspace)
+    dt = _dtype_code(out)
+    _expect(context_lens, torch.int32, 1, "context_lens")
+    S, H, D = out.shape
+    rc = lib().paged_attention_decode_merge(out.data_ptr(), context_lens.data_ptr(), S, H, D,
+                                            block_size, max_blocks_per_seq, dt,
+                                            workspace.data_ptr(), workspace.numel(), _stream(out))
+    check("paged_attention_decode_merge", rc)
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, block_size: int = 16):
+    """Scatter new tokens' K/V rows into their slots (in place)."""
+    _on_gpu(key, value, key_cache, value_cache, slot_mapping)
+    dt = _dtype_code(key, value, key_cache, value_cache)
+    _expect(slot_mapping, torch.int64, 1, "slot_mapping")
+    if key.dim() != 3 or key.shape != value.shape or key_cache.dim() != 4:
+        raise ValueError("key/value [T,H,D] and caches [NB,bs,H,D] expected")
+    T, H, D = key.shape
+    NB, bs, H2, D2 = key_cache.shape
+    if value_cache.shape != key_cache.shape or (H2, D2) != (H, D) or bs != block_size:
+        raise ValueError("key/value and cache shapes disagree")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping needs one entry per token")
+    rc = lib().reshape_and_cache(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                 value_cache.data_ptr(), slot_mapping.data_ptr(), T, H, D, NB,
+                                 block_size, dt, _stream(key))
+    check("reshape_and_cache", rc)
+
+
+def copy_blocks(key_cache, value_cache, block_mapping, block_size: int = 16):
+    """Copy whole blocks src -> dst in both pools (in place)."""
+    _on_gpu(key_cache, value_cache, block_mapping)
+    dt = _dtype_code(key_cache, value_cache)
+    _expect(block_mapping, torch.int32, 2, "block_mapping")
+    if key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("caches [NB,bs,H,D] expected")
+    if block_mapping.shape[0] and block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2]")
+    NB, bs, H, D = key_cache.shape
+    if bs != block_size:
+        raise ValueError("cache block size disagrees with block_size")
+    rc = lib().copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), block_mapping.data_ptr(),
+                           block_mapping.shape[0], H, D, NB, block_size, dt, _stream(key_cache))
+    check("copy_blocks", rc)

@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/paged_kv.h declares, and rejects invalid arguments with the documented
+status codes before any HIP call (fake device pointers are never dereferenced
+on those paths; calls that would launch are not made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_kv.h")
+
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6
+P = 0x10000        # fake, 16-byte aligned "device" pointer (never dereferenced)
+MIS = 0x10008      # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    from paged_kv_cache_159_amd import _lib
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                      text, flags=re.M)
+
+
+def test_header_declares_expected_functions():
+    from paged_kv_cache_159_amd._lib import EXPORTS
+    assert sorted(header_functions()) == sorted(EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.pkv_version() >= 100
+    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALIGN):
+        s = L.pkv_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert L.pkv_status_string(42).decode() == "unknown status"
+
+
+def test_workspace_size(L):
+    # one partition (<= 512 tokens): no workspace
+    assert L.paged_attention_workspace_size(4, 4, 64, 4, 16) == 0
+    assert L.paged_attention_workspace_size(64, 32, 128, 32, 16) == 0
+    # 128 blocks -> 4 partitions: (m, l) pairs padded to 256 B, then fp32 vectors
+    n = 64 * 32 * 4
+    want = ((n * 8 + 255) // 256) * 256 + n * 128 * 4
+    assert L.paged_attention_workspace_size(64, 32, 128, 128, 16) == want
+    # 2048 blocks -> 64 partitions
+    n = 8 * 32 * 64
+    assert L.paged_attention_workspace_size(8, 32, 128, 2048, 16) == ((n * 8 + 255) // 256) * 256 + n * 512
+    # invalid -> 0
+    assert L.paged_attention_workspace_size(8, 32, 96, 2048, 16) == 0
+    assert L.paged_attention_workspace_size(8, 32, 128, 2048, 8) == 0
+
+
+def _decode(L, fn="paged_attention_decode", **kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, cl=P, S=4, H=4, D=64, NB=32, bs=16, MB=4, scale=0.125,
+             dt=0, ws=0, wsb=0, stream=0)
+    a.update(kw)
+    return getattr(L, fn)(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["H"], a["D"],
+                          a["NB"], a["bs"], a["MB"], a["scale"], a["dt"], a["ws"], a["wsb"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["paged_attention_decode", "paged_attention_decode_partitions"])
+def test_decode_validation(L, fn):
+    assert _decode(L, fn, dt=2) == UNSUP
+    assert _decode(L, fn, bs=32) == UNSUP
+    assert _decode(L, fn, D=96) == UNSUP
+    assert _decode(L, fn, H=0) == SHAPE
+    assert _decode(L, fn, NB=0) == SHAPE
+    assert _decode(L, fn, S=-1) == SHAPE
+    assert _decode(L, fn, MB=0) == SHAPE
+    assert _decode(L, fn, MB=2 ** 28) == SHAPE             # MB * bs overflows int32
+    assert _decode(L, fn, scale=float("nan")) == SHAPE
+    assert _decode(L, fn, scale=float("inf")) == SHAPE
+    for name in ("out", "q", "k", "v", "bt", "cl"):
+        assert _decode(L, fn, **{name: 0}) == NULL, name
+    for name in ("out", "q", "k", "v"):
+        assert _decode(L, fn, **{name: MIS}) == ALIGN, name
+    assert _decode(L, fn, bt=P + 2) == ALIGN
+    # more than one partition needs a workspace of the right size
+    need = L.paged_attention_workspace_size(4, 4, 64, 64, 16)
+    assert need > 0
+    assert _decode(L, fn, MB=64) == WS
+    assert _decode(L, fn, MB=64, ws=P, wsb=need - 1) == WS
+    assert _decode(L, fn, MB=64, ws=MIS, wsb=need) == ALIGN
+    # zero sequences: valid, nothing launched
+    assert _decode(L, fn, S=0) == OK
+
+
+def test_merge_validation(L):
+    m = L.paged_attention_decode_merge
+    need = L.paged_attention_workspace_size(4, 4, 64, 64, 16)
+    assert m(P, P, 4, 4, 64, 16, 64, 0, 0, 0, 0) == WS
+    assert m(0, P, 4, 4, 64, 16, 64, 0, P, need, 0) == NULL
+    assert m(P, P, 4, 4, 64, 16, 64, 3, P, need, 0) == UNSUP
+    assert m(MIS, P, 4, 4, 64, 16, 64, 0, P, need, 0) == ALIGN
+    # one partition: nothing to merge, no launch
+    assert m(P, P, 4, 4, 64, 16, 4, 0, 0, 0, 0) == OK
+    assert m(P, P, 0, 4, 64, 16, 64, 0, P, need, 0) == OK
+
+
+def test_reshape_and_cache_validation(L):
+    f = L.reshape_and_cache
+    base = [P, P, P, P, P, 3, 4, 64, 32, 16, 0, 0]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(10, 5) == UNSUP
+    assert call(9, 8) == UNSUP
+    assert call(7, 80) == UNSUP
+    assert call(6, 0) == SHAPE
+    assert call(8, 0) == SHAPE
+    assert call(5, -1) == SHAPE
+    for i in range(5):
+        assert call(i, 0) == NULL
+    for i in range(4):
+        assert call(i, MIS) == ALIGN
+    assert call(4, P + 4) == ALIGN                 # int64 slots need 8-byte alignment
+    assert call(5, 0) == OK                        # no tokens: nothing launched
+
+
+def test_copy_blocks_validation(L):
+    f = L.copy_blocks
+    base = [P, P, P, 2, 4, 64, 32, 16, 0, 0]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(8, 7) == UNSUP
+    assert call(7, 4) == UNSUP
+    assert call(5, 32) == UNSUP
+    assert call(3, -1) == SHAPE
+    assert call(4, 0) == SHAPE
+    for i in range(3):
+        assert call(i, 0) == NULL
+    assert call(0, MIS) == ALIGN
+    assert call(2, P + 2) == ALIGN
+    assert call(3, 0) == OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import paged_kv_cache_159_amd as pkv
+    x = torch.zeros(2, 4, 64, dtype=torch.float16)
+    c = torch.zeros(4, 16, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        pkv.reshape_and_cache(x, x, c, c, torch.zeros(2, dtype=torch.int64))
+
+
+def test_binding_reports_status_as_error():
+    from paged_kv_cache_159_amd._lib import PagedKVError, check
+    with pytest.raises(PagedKVError, match="PKV_ERR_UNSUPPORTED"):
+        check("x", UNSUP)

@@ -6,4 +6,6 @@ arithmetic lives here.
 """
 
 from .allocator import BlockAllocator  # noqa: F401
-from .configs import BLOCK_SIZE, CONFIG_NAMES, Workload, make_config, poison_unused  # noqa: F401
+from .configs import (  # noqa: F401
+    BLOCK_SIZE, CONFIG_NAMES, Workload, make_config, make_decode_case, poison_unused,
+)

@@ -165,6 +165,19 @@ def _decode_batch(index, name, dtype, H, D, ctx, MB, streams, pool=None):
     return _finish(index, name, dtype, H, D, alloc, seqs, ctx, MB, streams, S, slots, [])
 
 
+def make_decode_case(ctx, num_heads: int, head_dim: int, dtype: str = "f16", seed: int = 0,
+                     max_blocks: int | None = None, pool: int | None = None) -> Workload:
+    """A decode step over the given context lengths (each sequence's last token
+    is written by the step), for edge-case tests. Same recipe as the numbered
+    workloads, seeded by ``seed``."""
+    st = np.random.SeedSequence(seed).spawn(8)
+    ctx = [int(c) for c in ctx]
+    if min(ctx) < 1:
+        raise ValueError("context lengths must be >= 1")
+    mb = max_blocks if max_blocks is not None else max(_blocks(c) for c in ctx)
+    return _decode_batch(0, "custom", dtype, num_heads, head_dim, ctx, mb, st, pool)
+
+
 def make_config(index: int) -> Workload:
     """Build workload ``index`` (1..5). Deterministic for a given index."""
     st = _seed_streams(index)
