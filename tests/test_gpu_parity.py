@@ -56,19 +56,38 @@ def oracle_step(w, pairs=None):
     return K, V, out
 
 
-def assert_attention_close(got, want, pairs=None, what=""):
+def half_ulp(x, dtype):
+    """Half the spacing of the output format at |x| (normal range; the
+    subnormal spacing below it)."""
+    mant, emin = (10, -14) if dtype == "f16" else (7, -126)
+    a = np.maximum(np.abs(x), 2.0 ** emin)
+    return 0.5 * np.exp2(np.floor(np.log2(a)) - mant)
+
+
+def assert_attention_close(got, want, pairs=None, what="", format_bound=None):
+    """Default: the 2e-3 max / 2e-4 mean bar. With ``format_bound`` (a dtype),
+    the per-element bound is the larger of 2e-3 and half an output ulp of the
+    value plus 1e-5 (fp32 arithmetic), and the mean bar is dropped: rounding
+    a bf16 output of magnitude >= 1 alone can exceed 2e-3 (half an ulp in
+    [1, 2) is 3.9e-3), which only happens for very short contexts."""
     if pairs is not None:
         got = np.stack([got[s, h] for s, h in pairs])
         want = np.stack([want[s, h] for s, h in pairs])
     assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
     err = np.abs(got - want)
     worst = np.unravel_index(np.argmax(err), err.shape)
-    say(f"{what}: max abs {err.max():.3e} at {worst}, mean abs {err.mean():.3e}")
-    assert err.max() <= MAX_ABS, f"{what}: max abs error {err.max():.3e}"
-    assert err.mean() <= MEAN_ABS, f"{what}: mean abs error {err.mean():.3e}"
+    say(f"{what}: max abs {err.max():.3e} at {worst} (value {want[worst]:.4f}), "
+        f"mean abs {err.mean():.3e}")
+    if format_bound is None:
+        assert err.max() <= MAX_ABS, f"{what}: max abs error {err.max():.3e}"
+        assert err.mean() <= MEAN_ABS, f"{what}: mean abs error {err.mean():.3e}"
+    else:
+        bound = np.maximum(MAX_ABS, half_ulp(np.maximum(np.abs(want), np.abs(got)), format_bound) + 1e-5)
+        bad = err > bound
+        assert not bad.any(), f"{what}: {bad.sum()} elements beyond half an output ulp + 1e-5"
 
 
-def check_full_step(w, pairs=None, check_caches=True, two_stage=False):
+def check_full_step(w, pairs=None, check_caches=True, two_stage=False, format_bound=None):
     say(f"config {w.index} {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} {w.dtype} "
         f"NB={w.num_blocks} MB={w.max_blocks_per_seq} T={len(w.slot_mapping)} "
         f"pairs={len(w.copy_pairs)} two_stage={two_stage}")
@@ -79,7 +98,7 @@ def check_full_step(w, pairs=None, check_caches=True, two_stage=False):
         assert np.array_equal(device_to_bits(dw.key_cache), K), "key cache differs"
         assert np.array_equal(device_to_bits(dw.value_cache), V), "value cache differs"
     got = device_to_float64(dw.out)
-    assert_attention_close(got, want, pairs, what=f"config {w.index}")
+    assert_attention_close(got, want, pairs, what=f"config {w.index}", format_bound=format_bound)
     return dw, got
 
 
@@ -188,8 +207,10 @@ def test_edge_context_lengths(dtype, head_dim):
     maximum (128 blocks); 3 heads so heads are not a power of two."""
     w = make_decode_case(EDGE_CTX, 3, head_dim, dtype, seed=head_dim + (dtype == "bf16"),
                          max_blocks=128)
-    check_full_step(w)
-    check_full_step(poison_unused(w), check_caches=False)
+    bound = "bf16" if dtype == "bf16" else None
+    _, clean = check_full_step(w, format_bound=bound)
+    _, poisoned = check_full_step(poison_unused(w), check_caches=False, format_bound=bound)
+    assert np.array_equal(clean, poisoned)
 
 
 def test_one_token_context_returns_v_exactly():
