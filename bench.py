@@ -46,24 +46,56 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 plain device copies of 1 GiB (the known-size reference for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": n,
+                      "bytes_written_per_dispatch": n, "dispatches": 5}), flush=True)
+
+
+def unique_kv_tokens(w):
+    """Distinct (physical block, row) token slots the decode reads: a block
+    shared by several sequences (a common prefix) is counted once, with the
+    most rows any of its readers uses."""
+    rows = np.zeros(w.num_blocks, dtype=np.int64)
+    for s in range(w.num_seqs):
+        ctx = int(w.context_lens[s])
+        n = (ctx + w.block_size - 1) // w.block_size
+        r = np.minimum(w.block_size, ctx - w.block_size * np.arange(n))
+        np.maximum.at(rows, w.block_tables[s, :n].astype(np.int64), r)
+    return int(rows.sum())
 
 
 def algorithmic_bytes(w):
     """Bytes the method must move, per launch, stated per unit:
-    decode: K+V of every valid token (num_heads*head_dim*2 B each for K and V:
-    16 KiB per token at 32 x 128 fp16), the query and output rows, the block
-    table entries of the valid blocks and the context lengths;
+    decode: K+V of every distinct valid token slot (num_heads*head_dim*2 B
+    each for K and V: 16 KiB per token at 32 x 128 fp16; a shared prefix block
+    counts once), the query and output rows, the block-table entries of the
+    valid blocks and the context lengths;
     write: each new token's K+V read once and written once, plus its slot;
-    copy: each CoW block read once and written once, K and V."""
+    copy: each CoW block read once and written once, K and V.
+    Also returns the logical decode bytes (every sequence's tokens counted)."""
     kvt = w.kv_bytes_per_token
     rowb = w.num_heads * w.head_dim * 2
     nblocks = int(((w.context_lens.astype(np.int64) + w.block_size - 1) // w.block_size).sum())
-    decode = w.total_context * kvt + 2 * w.num_seqs * rowb + 4 * nblocks + 4 * w.num_seqs
+    meta = 2 * w.num_seqs * rowb + 4 * nblocks + 4 * w.num_seqs
+    decode = unique_kv_tokens(w) * kvt + meta
+    logical = w.total_context * kvt + meta
     T = len(w.slot_mapping)
     write = 2 * T * kvt + 8 * T
     copy = len(w.copy_pairs) * (2 * 2 * w.block_size * rowb + 8)
-    return decode, write, copy
+    return decode, write, copy, logical
 
 
 def source_digest():
@@ -131,6 +163,10 @@ def main():
               "(--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
     import torch
     import paged_kv_cache_159_amd as pkv
     from workloads import make_config
@@ -156,7 +192,7 @@ def main():
     vcs = [dw.value_cache] + [dw.value_cache.clone() for _ in range(R - 1)]
     ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq, device=dev)
     outs = [torch.empty_like(dw.query) for _ in range(R)]
-    dec_b, write_b, copy_b = algorithmic_bytes(w)
+    dec_b, write_b, copy_b, logical_b = algorithmic_bytes(w)
     step_bytes = dec_b + write_b + copy_b
     has_copy = len(w.copy_pairs) > 0
     print(f"[bench] {R} pool replicas of {pool_bytes / 1e9:.2f} GB; algorithmic bytes/step: "
@@ -227,6 +263,7 @@ def main():
         "seqs_per_s": round(w.num_seqs / (ms * 1e-3), 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "decode_partition_us": round(dec_avg_us, 2),
+        "decode_logical_kv_gbs": round(logical_b / (dec_avg_us * 1e-6) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

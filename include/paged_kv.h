@@ -78,10 +78,11 @@ const char* pkv_status_string(int status);
 
 /*
  * Workspace bytes paged_attention_decode needs for these sizes: fp32 partial
- * results (running max, exponent sum and a head_dim vector) of every
- * 512-token context partition of every (sequence, head). Returns 0 when no
- * sequence can span more than one partition (max_blocks_per_seq*block_size
- * <= 512) or when the arguments are invalid.
+ * results (running max, exponent sum and a head_dim vector) of every context
+ * partition of every (sequence, head). A partition is 256 tokens when
+ * max_blocks_per_seq*block_size <= 4096, else 512 tokens. Returns 0 when no
+ * sequence can span more than one partition or when the arguments are
+ * invalid.
  */
 size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
                                       int max_blocks_per_seq, int block_size);
@@ -94,8 +95,9 @@ size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
  *     out[s][h] = sum_t softmax(x)_t * V_t
  * where K_t and V_t are token t's rows of head h, found through block_tables[s].
  * Accumulation is fp32; the output is rounded to nearest-even into `dtype`.
- * Contexts longer than 512 tokens are split into 512-token partitions whose
- * partial results are merged by log-sum-exp; the reduction order depends only
+ * Contexts are split into partitions of 256 tokens (512 when
+ * max_blocks_per_seq*block_size > 4096) whose partial results are merged by
+ * log-sum-exp; the reduction order depends only
  * on logical token positions, so relabelling physical blocks leaves `out`
  * bit-identical.
  * `workspace` (>= paged_attention_workspace_size(...) bytes, any content) may
@@ -113,7 +115,7 @@ int paged_attention_decode(void* out, const void* query,
 
 /*
  * First of the two launches of paged_attention_decode: one workgroup per
- * (sequence, head, 512-token partition). Sequences whose context fits one
+ * (sequence, context partition, group of heads). Sequences whose context fits one
  * partition get their final `out` here; the others leave partials in
  * `workspace`. Exposed so that callers can schedule or time the two launches
  * separately; the arguments mean the same as for paged_attention_decode.
@@ -131,7 +133,7 @@ int paged_attention_decode_partitions(void* out, const void* query,
  * paged_attention_decode_partitions for sequences longer than one partition,
  * writing their `out`. Must follow that call on the same stream, with the
  * same out, context_lens, sizes and workspace. Does nothing (and launches
- * nothing) when max_blocks_per_seq*block_size <= 512.
+ * nothing) when max_blocks_per_seq*block_size <= 256.
  */
 int paged_attention_decode_merge(void* out, const int32_t* context_lens,
                                  int num_seqs, int num_heads, int head_dim,

@@ -31,7 +31,8 @@ int check_layout(int dtype, int block_size, int num_heads, int head_dim, int num
 
 int num_partitions(int max_blocks_per_seq, int block_size) {
   const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
-  return (int)((tokens + pkv::kPartitionTokens - 1) / pkv::kPartitionTokens);
+  const int pt = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
+  return (int)((tokens + pt - 1) / pt);
 }
 
 // Validation shared by the decode entry points. Fills *parts and *need.
@@ -85,6 +86,7 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->head_dim = head_dim;
   a->max_blocks_per_seq = max_blocks_per_seq;
   a->num_parts = parts;
+  a->part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
   a->scale = scale;
   a->dtype = dtype;
   a->ws_ml = nullptr;
@@ -160,6 +162,7 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens, int num
   a.head_dim = head_dim;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_parts = parts;
+  a.part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
   a.dtype = dtype;
   pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a.ws_ml, &a.ws_o);
   return status_of(pkv::launch_decode_merge(a, static_cast<hipStream_t>(stream)));

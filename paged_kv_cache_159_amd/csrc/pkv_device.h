@@ -8,8 +8,6 @@
 
 namespace pkv {
 
-// Tokens per context partition of the decode kernels (32 blocks of 16).
-constexpr int kPartitionTokens = 512;
 constexpr int kBlockSize = 16;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -22,12 +22,16 @@ struct DecodeArgs {
   int num_heads;
   int head_dim;
   int max_blocks_per_seq;
+  int part_tokens;      // tokens per context partition (decode_partition_tokens)
   int num_parts;        // partitions per (sequence, head) in the workspace layout
   float scale;
   int dtype;            // 0 fp16, 1 bf16
   float* ws_ml;         // [num_seqs][num_heads][num_parts][2] (running max, exp sum), log2 domain
   float* ws_o;          // [num_seqs][num_heads][num_parts][head_dim] normalised partial outputs
 };
+
+// Tokens per context partition for these sizes (64 or 256).
+int decode_partition_tokens(int max_blocks_per_seq, int block_size);
 
 // Workspace layout shared by the two decode launches.
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int num_parts);

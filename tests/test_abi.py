@@ -48,19 +48,25 @@ def test_version_and_status_strings(L):
     assert L.pkv_status_string(42).decode() == "unknown status"
 
 
+def _expected_workspace(S, H, D, MB, bs=16):
+    """The documented rule: 256-token partitions up to 4096 tokens per table,
+    512 beyond; (max, sum) pairs padded to 256 bytes, then fp32 vectors."""
+    tokens = MB * bs
+    pt = 256 if tokens <= 4096 else 512
+    P = -(-tokens // pt)
+    if P <= 1:
+        return 0
+    n = S * H * P
+    return ((n * 8 + 255) // 256) * 256 + n * D * 4
+
+
 def test_workspace_size(L):
-    # one partition (<= 512 tokens): no workspace
-    assert L.paged_attention_workspace_size(4, 4, 64, 4, 16) == 0
-    assert L.paged_attention_workspace_size(64, 32, 128, 32, 16) == 0
-    # 128 blocks -> 4 partitions: (m, l) pairs padded to 256 B, then fp32 vectors
-    n = 64 * 32 * 4
-    want = ((n * 8 + 255) // 256) * 256 + n * 128 * 4
-    assert L.paged_attention_workspace_size(64, 32, 128, 128, 16) == want
-    # 2048 blocks -> 64 partitions
-    n = 8 * 32 * 64
-    assert L.paged_attention_workspace_size(8, 32, 128, 2048, 16) == ((n * 8 + 255) // 256) * 256 + n * 512
-    # invalid -> 0
-    assert L.paged_attention_workspace_size(8, 32, 96, 2048, 16) == 0
+    assert L.paged_attention_workspace_size(4, 4, 64, 16, 16) == 0    # 256 tokens: one partition
+    for S, H, D, MB in ((4, 4, 64, 17), (64, 32, 128, 32), (64, 32, 128, 128), (64, 32, 128, 256),
+                        (64, 32, 128, 257), (8, 32, 128, 2048), (3, 5, 64, 1000)):
+        assert L.paged_attention_workspace_size(S, H, D, MB, 16) == _expected_workspace(S, H, D, MB)
+    assert _expected_workspace(64, 32, 128, 128) == 64 * 32 * 8 * 8 + 64 * 32 * 8 * 512
+    assert L.paged_attention_workspace_size(8, 32, 96, 2048, 16) == 0  # invalid -> 0
     assert L.paged_attention_workspace_size(8, 32, 128, 2048, 8) == 0
 
 
@@ -103,11 +109,12 @@ def test_decode_validation(L, fn):
 def test_merge_validation(L):
     m = L.paged_attention_decode_merge
     need = L.paged_attention_workspace_size(4, 4, 64, 64, 16)
+    assert need > 0
     assert m(P, P, 4, 4, 64, 16, 64, 0, 0, 0, 0) == WS
     assert m(0, P, 4, 4, 64, 16, 64, 0, P, need, 0) == NULL
     assert m(P, P, 4, 4, 64, 16, 64, 3, P, need, 0) == UNSUP
     assert m(MIS, P, 4, 4, 64, 16, 64, 0, P, need, 0) == ALIGN
-    # one partition: nothing to merge, no launch
+    # one partition (<= 256 tokens): nothing to merge, no launch
     assert m(P, P, 4, 4, 64, 16, 4, 0, 0, 0, 0) == OK
     assert m(P, P, 0, 4, 64, 16, 64, 0, P, need, 0) == OK
 
