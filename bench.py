@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ungrouped", action="store_true",
+                    help="shared-prefix workload: use the plain decode instead of the grouped one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -199,6 +201,13 @@ def main():
           f"decode {dec_b} write {write_b} copy {copy_b}", file=sys.stderr, flush=True)
 
     ev = []
+    grouped = w.group_start is not None and not args.ungrouped
+    if grouped:
+        gs = torch.from_numpy(w.group_start).to(dev)
+        sb = torch.from_numpy(w.shared_blocks).to(dev)
+        gws = torch.empty(max(pkv.grouped_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                         w.max_blocks_per_seq), 16),
+                          dtype=torch.uint8, device=dev)
 
     def step(i, record):
         r = i % R
@@ -210,6 +219,14 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
+        if grouped:
+            # shared-prefix MFMA launch + tail partitions + merge, timed together
+            pkv.paged_attention_decode_grouped(outs[r], dw.query, kc, vc, dw.block_tables,
+                                               dw.context_lens, gs, sb, w.scale, workspace=gws)
+            if record:
+                e1.record()
+                ev.append((e0, e1))
+            return
         pkv.paged_attention_decode_partitions(outs[r], dw.query, kc, vc, dw.block_tables,
                                               dw.context_lens, w.scale, ws)
         if record:
@@ -271,7 +288,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_partition_kernel",
+            "kernel": "grouped decode (shared-prefix MFMA + tail partitions + merge)" if grouped
+                      else "decode_partition_kernel",
             "bytes_per_launch": dec_b,
         },
     }

@@ -46,7 +46,8 @@
  * device synchronisation): block-table entries that are read lie in
  * [0, num_blocks); 1 <= context_lens[s] <= max_blocks_per_seq*block_size;
  * slots are < num_blocks*block_size and unique within a call; copy pairs have
- * unique destinations that are not sources in the same call.
+ * unique destinations that are not sources in the same call; for the grouped
+ * call, the group constraints stated at paged_attention_decode_grouped.
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H
@@ -139,6 +140,43 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens,
                                  int num_seqs, int num_heads, int head_dim,
                                  int block_size, int max_blocks_per_seq, int dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes paged_attention_decode_grouped needs: fp32 partials of every
+ * shared-prefix chunk (4 blocks) and every tail partition of every (sequence,
+ * head). Returns 0 when the arguments are invalid.
+ */
+size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                              int max_blocks_per_seq, int block_size);
+
+/*
+ * Decode attention for sequences that share prefix blocks, e.g. the samples of
+ * one prompt in parallel sampling or the beams of a beam search [P2 "Copy-on-
+ * Write共享解码的显存优化原理": sequences with a common prefix map it to the same
+ * physical blocks; P4 "Memory Sharing与写时复制"]. Same result as
+ * paged_attention_decode (within rounding; the summation order differs), but
+ * each shared block is read once per group and its attention for all the
+ * group's queries runs on the MFMA matrix cores.
+ *   group_start    int32 [num_groups + 1], device: group g is sequences
+ *                  [group_start[g], group_start[g+1]); group_start[0] = 0,
+ *                  nondecreasing, group_start[num_groups] = num_seqs.
+ *   shared_blocks  int32 [num_groups], device: the first shared_blocks[g]
+ *                  block-table entries are identical for every member of
+ *                  group g and are full blocks of every member's context
+ *                  (shared_blocks[g] * block_size <= context_lens[s]).
+ * Groups of any size are allowed (queries are processed 16 at a time); a
+ * group with shared_blocks 0, or of one sequence, takes the ordinary path.
+ * Three launches on `stream`: shared-prefix chunks, tail partitions, merge.
+ * `workspace` needs paged_attention_grouped_workspace_size(...) bytes.
+ */
+int paged_attention_decode_grouped(void* out, const void* query,
+                                   const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* group_start, const int32_t* shared_blocks,
+                                   int num_groups, int num_seqs, int num_heads, int head_dim,
+                                   int num_blocks, int block_size, int max_blocks_per_seq,
+                                   float scale, int dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * Slot-mapped cache write [P2 "Copy-on-Write共享解码的显存优化原理": the new

@@ -10,7 +10,9 @@ from ._lib import PagedKVError, lib  # noqa: F401
 from .ops import (  # noqa: F401
     alloc_workspace,
     copy_blocks,
+    grouped_workspace_size,
     paged_attention_decode,
+    paged_attention_decode_grouped,
     paged_attention_decode_merge,
     paged_attention_decode_partitions,
     reshape_and_cache,

@@ -21,6 +21,8 @@ EXPORTS = (
     "paged_attention_decode",
     "paged_attention_decode_partitions",
     "paged_attention_decode_merge",
+    "paged_attention_grouped_workspace_size",
+    "paged_attention_decode_grouped",
     "reshape_and_cache",
     "copy_blocks",
 )
@@ -44,6 +46,9 @@ _SIGNATURES = {
     "paged_attention_decode_partitions": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i,
                                                _p, _z, _p]),
     "paged_attention_decode_merge": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _p, _z, _p]),
+    "paged_attention_grouped_workspace_size": (_z, [_i, _i, _i, _i, _i]),
+    "paged_attention_decode_grouped": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                            _f, _i, _p, _z, _p]),
     "reshape_and_cache": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "copy_blocks": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
 }

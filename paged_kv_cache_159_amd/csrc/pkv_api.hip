@@ -89,9 +89,34 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
   a->scale = scale;
   a->dtype = dtype;
+  a->tail_parts = parts;
+  a->slot_base = 0;
+  a->group_start = nullptr;
+  a->shared_blocks = nullptr;
+  a->num_groups = 0;
   a->ws_ml = nullptr;
   a->ws_o = nullptr;
   if (need) pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a->ws_ml, &a->ws_o);
+  return PKV_OK;
+}
+
+// Partial slots of the grouped call: shared-prefix chunks, then tail partitions.
+void grouped_slots(int max_blocks_per_seq, int block_size, int* chunk_slots, int* tail_parts) {
+  *chunk_slots = (max_blocks_per_seq + pkv::kSharedChunkBlocks - 1) / pkv::kSharedChunkBlocks;
+  *tail_parts = num_partitions(max_blocks_per_seq, block_size);
+}
+
+int check_grouped(int num_seqs, int num_heads, int head_dim, int block_size,
+                  int max_blocks_per_seq, int num_groups, int* chunk_slots, int* tail_parts,
+                  size_t* need) {
+  if (num_seqs < 0 || max_blocks_per_seq < 1 || num_groups < 0) return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && num_groups < 1) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxGrid) return PKV_ERR_SHAPE;
+  grouped_slots(max_blocks_per_seq, block_size, chunk_slots, tail_parts);
+  const int64_t slots = (int64_t)*chunk_slots + *tail_parts;
+  if ((int64_t)num_seqs * num_heads * slots > kMaxGrid) return PKV_ERR_SHAPE;
+  if ((int64_t)num_groups * (*chunk_slots) * num_heads > kMaxGrid) return PKV_ERR_SHAPE;
+  *need = pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)slots);
   return PKV_OK;
 }
 
@@ -162,6 +187,7 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens, int num
   a.head_dim = head_dim;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_parts = parts;
+  a.tail_parts = parts;
   a.part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
   a.dtype = dtype;
   pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a.ws_ml, &a.ws_o);
@@ -181,6 +207,71 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = status_of(pkv::launch_decode_partitions(a, st));
   if (rc || a.num_parts <= 1) return rc;
+  return status_of(pkv::launch_decode_merge(a, st));
+}
+
+size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                              int max_blocks_per_seq, int block_size) {
+  if (check_layout(PKV_F16, block_size, num_heads, head_dim, 1)) return 0;
+  int cs = 0, tp = 0;
+  size_t need = 0;
+  if (check_grouped(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, 1, &cs, &tp,
+                    &need))
+    return 0;
+  return need;
+}
+
+int paged_attention_decode_grouped(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, const int32_t* group_start,
+                                   const int32_t* shared_blocks, int num_groups, int num_seqs,
+                                   int num_heads, int head_dim, int num_blocks, int block_size,
+                                   int max_blocks_per_seq, float scale, int dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, num_blocks);
+  if (rc) return rc;
+  int chunk_slots = 0, tail_parts = 0;
+  size_t need = 0;
+  rc = check_grouped(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, num_groups,
+                     &chunk_slots, &tail_parts, &need);
+  if (rc) return rc;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !group_start || !shared_blocks)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(group_start) ||
+      !aligned4(shared_blocks))
+    return PKV_ERR_ALIGN;
+  rc = check_workspace(workspace, workspace_bytes, need);
+  if (rc) return rc;
+  pkv::DecodeArgs a = {};
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
+  a.num_parts = chunk_slots + tail_parts;
+  a.tail_parts = tail_parts;
+  a.slot_base = chunk_slots;
+  a.group_start = group_start;
+  a.shared_blocks = shared_blocks;
+  a.num_groups = num_groups;
+  a.scale = scale;
+  a.dtype = dtype;
+  pkv::decode_workspace_split(workspace, num_seqs, num_heads, a.num_parts, &a.ws_ml, &a.ws_o);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = status_of(pkv::launch_decode_shared(a, st));
+  if (rc) return rc;
+  rc = status_of(pkv::launch_decode_partitions(a, st));
+  if (rc) return rc;
   return status_of(pkv::launch_decode_merge(a, st));
 }
 

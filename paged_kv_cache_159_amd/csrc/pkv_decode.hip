@@ -43,7 +43,11 @@ namespace pkv {
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = kBlockSize / kWaves;  // rows of a block each wave reads
 
-template <typename T, int D, int PT>
+// TAIL = true is the grouped call's second launch: each sequence starts after
+// its group's shared blocks (those are handled by the shared-prefix kernel),
+// its partitions go to partial slots slot_base + p, and every partition
+// writes a partial (the merge always runs).
+template <typename T, int D, int PT, bool TAIL>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         float* __restrict__ ws_o, const uint16_t* __restrict__ query,
@@ -51,7 +55,10 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         const uint16_t* __restrict__ value_cache,
                         const int32_t* __restrict__ block_tables,
                         const int32_t* __restrict__ context_lens, int num_seqs, int num_heads,
-                        int max_blocks, int num_parts, float scale_log2) {
+                        int max_blocks, int num_parts, float scale_log2,
+                        const int32_t* __restrict__ group_start,
+                        const int32_t* __restrict__ shared_blocks, int num_groups,
+                        int slot_base) {
   using E = Elem<T>;
   constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
   constexpr int HG = 64 / LPR;       // heads per wave-wide load
@@ -64,7 +71,9 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
   const int s = sp % num_seqs;
   const int p = sp / num_seqs;
   const int ctx = context_lens[s];
-  const int tok_begin = p * PT;
+  int tok0 = 0;   // first token this launch covers for sequence s
+  if constexpr (TAIL) tok0 = shared_blocks[group_of(s, group_start, num_groups)] * kBlockSize;
+  const int tok_begin = tok0 + p * PT;
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + PT);
   const int blk_begin = tok_begin / kBlockSize;
@@ -155,7 +164,7 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
     s_l[wave][hl] = l;
   }
   __syncthreads();
-  const int parts_s = (ctx + PT - 1) / PT;
+  const int parts_s = TAIL ? 0 : (ctx + PT - 1) / PT;
   for (int o = threadIdx.x; o < HG * D; o += kWaves * 64) {
     const int ol = o / D;
     const int d = o % D;
@@ -174,7 +183,7 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
     if (parts_s == 1) {
       out[((size_t)s * H + oh) * D + d] = E::round(val / L);
     } else {
-      const size_t pi = ((size_t)s * H + oh) * num_parts + p;
+      const size_t pi = ((size_t)s * H + oh) * num_parts + slot_base + p;
       ws_o[pi * D + d] = val / L;
       if (d == 0) {
         ws_ml[pi * 2] = M;
@@ -184,32 +193,47 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
   }
 }
 
-// Log-sum-exp merge of the partition partials of one (sequence, head).
-// 256 threads: thread (k, d) sums partitions k, k + K, ... for output element
-// d (K = 256 / D partition lanes), then the K partial sums meet in LDS. The
-// loads of different partitions are independent, so many are in flight.
+// Log-sum-exp merge of the partials of one (sequence, head). Partials live in
+// slots [0, n0) and [slot_base, slot_base + n1) of the sequence's slot row
+// (the plain call uses only the first range; the grouped call puts the
+// shared-prefix chunks in the first and the tail partitions in the second).
+// 256 threads: thread (k, d) sums slots k, k + K, ... for output element d
+// (K = 256 / D), then the K partial sums meet in LDS. The loads of different
+// slots are independent, so many are in flight.
 constexpr int kMergeThreads = 256;
 
-template <typename T, int D>
+template <typename T, int D, bool GROUPED>
 __global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
                     const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens,
-                    int num_heads, int num_parts, int part_tokens) {
+                    int num_heads, int num_parts, int part_tokens,
+                    const int32_t* __restrict__ group_start,
+                    const int32_t* __restrict__ shared_blocks, int num_groups, int chunk_blocks,
+                    int slot_base) {
   using E = Elem<T>;
   constexpr int K = kMergeThreads / D;
   const int H = num_heads;
   const int h = blockIdx.x % H;
   const int s = blockIdx.x / H;
   const int ctx = context_lens[s];
-  const int np = (ctx + part_tokens - 1) / part_tokens;
-  if (np <= 1) return;
+  int n0, n1;
+  if constexpr (GROUPED) {
+    const int sb = shared_blocks[group_of(s, group_start, num_groups)];
+    n0 = (sb + chunk_blocks - 1) / chunk_blocks;
+    n1 = (ctx - sb * kBlockSize + part_tokens - 1) / part_tokens;
+  } else {
+    n0 = (ctx + part_tokens - 1) / part_tokens;
+    n1 = 0;
+    if (n0 <= 1) return;  // written directly by the partition launch
+  }
+  const int n = n0 + n1;
+  auto slot = [&](int i) { return i < n0 ? i : slot_base + (i - n0); };
   const size_t base = ((size_t)s * H + h) * num_parts;
   const int d = threadIdx.x % D;
   const int k = threadIdx.x / D;
   __shared__ float s_red[kMergeThreads];
-  // global max of the partition maxima
   float M = -INFINITY;
-  for (int p = threadIdx.x; p < np; p += kMergeThreads) M = fmaxf(M, ws_ml[(base + p) * 2]);
+  for (int i = threadIdx.x; i < n; i += kMergeThreads) M = fmaxf(M, ws_ml[(base + slot(i)) * 2]);
   s_red[threadIdx.x] = M;
   __syncthreads();
   for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
@@ -220,10 +244,11 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
   __syncthreads();
   float L = 0.f, o = 0.f;
 #pragma unroll 4
-  for (int p = k; p < np; p += K) {
-    const float cw = ws_ml[(base + p) * 2 + 1] * fast_exp2(ws_ml[(base + p) * 2] - M);
+  for (int i = k; i < n; i += K) {
+    const size_t pi = base + slot(i);
+    const float cw = ws_ml[pi * 2 + 1] * fast_exp2(ws_ml[pi * 2] - M);
     L += cw;
-    o += cw * ws_o[(base + p) * D + d];
+    o += cw * ws_o[pi * D + d];
   }
   __shared__ float s_o[kMergeThreads], s_l[K];
   s_o[threadIdx.x] = o;
@@ -264,32 +289,43 @@ void decode_workspace_split(void* ws, int num_seqs, int num_heads, int num_parts
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int D, int PT>
+template <typename T, int D, int PT, bool TAIL>
 hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
   constexpr int HG = 64 / (D / 8);
   const unsigned groups = (unsigned)(a.num_heads + HG - 1) / HG;
-  const unsigned grid = (unsigned)a.num_seqs * groups * a.num_parts;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, PT>), dim3(grid), dim3(kWaves * 64), 0, st,
+  const unsigned grid = (unsigned)a.num_seqs * groups * (unsigned)a.tail_parts;
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, PT, TAIL>), dim3(grid), dim3(kWaves * 64), 0, st,
                      static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o,
                      static_cast<const uint16_t*>(a.query),
                      static_cast<const uint16_t*>(a.key_cache),
                      static_cast<const uint16_t*>(a.value_cache), a.block_tables, a.context_lens,
                      a.num_seqs, a.num_heads, a.max_blocks_per_seq, a.num_parts,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, a.group_start, a.shared_blocks, a.num_groups, a.slot_base);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t partitions_d(const DecodeArgs& a, hipStream_t st) {
-  return a.part_tokens == 256 ? partitions_t<T, D, 256>(a, st) : partitions_t<T, D, 512>(a, st);
+  const bool tail = a.group_start != nullptr;
+  if (a.part_tokens == 256)
+    return tail ? partitions_t<T, D, 256, true>(a, st) : partitions_t<T, D, 256, false>(a, st);
+  return tail ? partitions_t<T, D, 512, true>(a, st) : partitions_t<T, D, 512, false>(a, st);
 }
 
 template <typename T, int D>
 hipError_t merge_t(const DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.num_seqs * a.num_heads;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(grid), dim3(kMergeThreads), 0, st,
-                     static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
-                     a.num_parts, a.part_tokens);
+  if (a.group_start != nullptr) {
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, true>), dim3(grid), dim3(kMergeThreads), 0, st,
+                       static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
+                       a.num_parts, a.part_tokens, a.group_start, a.shared_blocks, a.num_groups,
+                       kSharedChunkBlocks, a.slot_base);
+  } else {
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, false>), dim3(grid), dim3(kMergeThreads), 0, st,
+                       static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
+                       a.num_parts, a.part_tokens, a.group_start, a.shared_blocks, a.num_groups,
+                       kSharedChunkBlocks, 0);
+  }
   return hipGetLastError();
 }
 }  // namespace

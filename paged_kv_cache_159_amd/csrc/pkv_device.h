@@ -80,4 +80,16 @@ __device__ __forceinline__ float group_sum(float x) {
 // 2^x with the hardware instruction (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Group of sequence s: the g with group_start[g] <= s < group_start[g + 1]
+// (binary search; group_start is nondecreasing from 0 to num_seqs).
+__device__ __forceinline__ int group_of(int s, const int32_t* __restrict__ group_start,
+                                        int num_groups) {
+  int lo = 0, hi = num_groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (group_start[mid] <= s) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 }  // namespace pkv

@@ -11,6 +11,9 @@ namespace pkv {
 // copy_blocks: 16-byte vectors one workgroup copies (256 threads x 4 = 16 KiB).
 constexpr int kCopyVecsPerGroup = 1024;
 
+// Grouped decode: shared-prefix blocks per workgroup of the shared-prefix kernel.
+constexpr int kSharedChunkBlocks = 4;
+
 struct DecodeArgs {
   void* out;
   const void* query;
@@ -23,7 +26,12 @@ struct DecodeArgs {
   int head_dim;
   int max_blocks_per_seq;
   int part_tokens;      // tokens per context partition (decode_partition_tokens)
-  int num_parts;        // partitions per (sequence, head) in the workspace layout
+  int num_parts;        // partial slots per (sequence, head) in the workspace layout
+  int tail_parts;       // partitions per sequence the partition launch covers
+  int slot_base;        // first slot of those partitions (grouped call: after the shared chunks)
+  const int32_t* group_start;    // grouped call only (else nullptr): [num_groups + 1]
+  const int32_t* shared_blocks;  // grouped call only: [num_groups]
+  int num_groups;
   float scale;
   int dtype;            // 0 fp16, 1 bf16
   float* ws_ml;         // [num_seqs][num_heads][num_parts][2] (running max, exp sum), log2 domain
@@ -40,6 +48,8 @@ void decode_workspace_split(void* ws, int num_seqs, int num_heads, int num_parts
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+// Grouped call, first launch: the shared-prefix blocks of every group.
+hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int64_t* slot_mapping, int num_tokens,

@@ -100,6 +100,37 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     return out
 
 
+def grouped_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, block_size: int = 16) -> int:
+    return int(lib().paged_attention_grouped_workspace_size(num_seqs, num_heads, head_dim,
+                                                            max_blocks_per_seq, block_size))
+
+
+def paged_attention_decode_grouped(out, query, key_cache, value_cache, block_tables, context_lens,
+                                   group_start, shared_blocks, scale: float, block_size: int = 16,
+                                   workspace=None) -> torch.Tensor:
+    """Decode attention with shared prefix blocks read once per group (MFMA).
+    group_start: int32 [G+1]; shared_blocks: int32 [G] (see include/paged_kv.h)."""
+    dt, S, H, D, NB, MB = _decode_args(out, query, key_cache, value_cache, block_tables,
+                                       context_lens, block_size)
+    _on_gpu(out, group_start, shared_blocks)
+    _expect(group_start, torch.int32, 1, "group_start")
+    _expect(shared_blocks, torch.int32, 1, "shared_blocks")
+    G = shared_blocks.shape[0]
+    if group_start.shape[0] != G + 1:
+        raise ValueError("group_start needs num_groups + 1 entries")
+    if workspace is None:
+        n = grouped_workspace_size(S, H, D, MB, block_size)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=out.device)
+    rc = lib().paged_attention_decode_grouped(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), group_start.data_ptr(),
+        shared_blocks.data_ptr(), G, S, H, D, NB, block_size, MB, float(scale), dt,
+        workspace.data_ptr(), workspace.numel(), _stream(out))
+    check("paged_attention_decode_grouped", rc)
+    return out
+
+
 def paged_attention_decode_partitions(out, query, key_cache, value_cache, block_tables,
                                       context_lens, scale: float, workspace,
                                       block_size: int = 16) -> None:

@@ -258,3 +258,93 @@ def test_copy_blocks_random_pairs_bit_exact():
     K, V = oracle.copy_blocks(w.key_cache, w.value_cache, pairs)
     assert np.array_equal(device_to_bits(dw.key_cache), K)
     assert np.array_equal(device_to_bits(dw.value_cache), V)
+
+
+# ------------------------------------------------------------ grouped (shared prefix)
+
+def grouped_step(w, dw, shared_blocks=None, group_start=None):
+    pkv = _pkv()
+    if len(w.copy_pairs):
+        pkv.copy_blocks(dw.key_cache, dw.value_cache, dw.copy_pairs)
+    pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
+    gs = torch.from_numpy(np.ascontiguousarray(w.group_start if group_start is None else group_start,
+                                               dtype=np.int32)).cuda()
+    sb = torch.from_numpy(np.ascontiguousarray(w.shared_blocks if shared_blocks is None
+                                               else shared_blocks, dtype=np.int32)).cuda()
+    pkv.paged_attention_decode_grouped(dw.out, dw.query, dw.key_cache, dw.value_cache,
+                                       dw.block_tables, dw.context_lens, gs, sb, w.scale)
+    torch.cuda.synchronize()
+
+
+def check_grouped(w, shared_blocks=None, group_start=None, format_bound=None, check_caches=True):
+    say(f"grouped {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} {w.dtype} "
+        f"groups={len(w.group_start if group_start is None else group_start) - 1} "
+        f"shared={(w.shared_blocks if shared_blocks is None else shared_blocks)[:4]}")
+    dw = upload(w)
+    grouped_step(w, dw, shared_blocks, group_start)
+    K, V, want = oracle_step(w)
+    if check_caches:
+        assert np.array_equal(device_to_bits(dw.key_cache), K), "key cache differs"
+        assert np.array_equal(device_to_bits(dw.value_cache), V), "value cache differs"
+    got = device_to_float64(dw.out)
+    assert_attention_close(got, want, what=f"grouped {w.name}", format_bound=format_bound)
+    dw2 = upload(w)
+    gpu_step(w, dw2)
+    plain = device_to_float64(dw2.out)
+    diff = np.abs(got - plain)
+    say(f"grouped vs ungrouped: max {diff.max():.3e} mean {diff.mean():.3e}")
+    if format_bound is None:
+        assert diff.max() <= MAX_ABS
+    return got
+
+
+def test_grouped_shared_prefix():
+    """16 prompts x 8 samples, bf16: 20 shared blocks per group on MFMA, tails
+    and the CoW-copied partial block on the partition kernel, one merge."""
+    check_grouped(make_config(4))
+
+
+def test_grouped_canaries_not_read():
+    w = make_config(4)
+    clean = check_grouped(w)
+    poisoned = check_grouped(poison_unused(w), check_caches=True)
+    assert np.array_equal(clean, poisoned)
+
+
+def test_grouped_large_groups_head_dim_64():
+    """Groups of 20 (two 16-query tiles), a full-block prefix (no CoW), some
+    samples with no suffix (whole context shared), 3 heads x 64, fp16."""
+    from workloads import make_shared_case
+    check_grouped(make_shared_case(2, 20, 80, 0, 30, 3, 64, "f16", seed=5))
+
+
+def test_grouped_fully_shared_no_tail():
+    from workloads import make_shared_case
+    w = make_shared_case(3, 4, 64, 0, 0, 4, 128, "bf16", seed=6)
+    assert (w.context_lens == 64).all() and (w.shared_blocks == 4).all()
+    check_grouped(w, format_bound="bf16")
+
+
+def test_grouped_without_shared_blocks_matches_plain():
+    """shared_blocks = 0: everything runs through the tail partitions."""
+    w = make_config(4)
+    check_grouped(w, shared_blocks=np.zeros(16, np.int32))
+
+
+def test_grouped_singleton_groups():
+    """One sequence per group, each sharing its own full blocks with itself:
+    the MFMA path with a single query per tile."""
+    w = make_decode_case([17, 64, 300, 1000, 2048, 33], 4, 128, "f16", seed=21, max_blocks=128)
+    gs = np.arange(w.num_seqs + 1, dtype=np.int32)
+    sb = ((w.context_lens - 1) // 16).astype(np.int32)
+    check_grouped(w, shared_blocks=sb, group_start=gs)
+
+
+def test_grouped_deterministic():
+    w = make_config(4)
+    dw = upload(w)
+    grouped_step(w, dw)
+    a = device_to_bits(dw.out)
+    dw2 = upload(w)
+    grouped_step(w, dw2)
+    assert np.array_equal(device_to_bits(dw2.out), a)

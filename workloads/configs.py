@@ -199,17 +199,29 @@ def make_config(index: int) -> Workload:
     raise ValueError(f"no workload {index}")
 
 
-def _shared_prefix(st) -> Workload:
-    prompts, samples, prefix, H, D = 16, 8, 328, 32, 128
-    suffix = np.random.Generator(np.random.PCG64(st[0])).integers(1, 256, size=prompts * samples,
+def _shared_prefix(st, index=4, name=CONFIG_NAMES[4], prompts=16, samples=8, prefix=328,
+                   suffix_lo=1, suffix_hi=256, H=32, D=128, dtype="bf16") -> Workload:
+    """Each prompt's prefix is allocated once and forked to its samples
+    (refcount = samples); then every sample appends its own suffix in index
+    order, copying the shared, partly filled last prefix block on its first
+    write while that block is still shared."""
+    suffix = np.random.Generator(np.random.PCG64(st[0])).integers(suffix_lo, suffix_hi,
+                                                                 size=prompts * samples,
                                                                  endpoint=True)
     ctx = prefix + suffix
-    prefix_blocks = _blocks(prefix)                      # 21, the last one partly filled
-    full_prefix_blocks = prefix // BLOCK_SIZE            # 20
-    # blocks in use at the end: one prefix per prompt, one CoW copy for every
-    # sample but the last of each prompt, and each sample's own further blocks
-    needed = prompts * prefix_blocks + prompts * (samples - 1) + sum(
-        _blocks(int(c)) - prefix_blocks for c in ctx)
+    prefix_blocks = _blocks(prefix)
+    full_prefix_blocks = prefix // BLOCK_SIZE
+    partial = prefix % BLOCK_SIZE != 0
+    # blocks in use at the end: one prefix per prompt, a CoW copy of a partly
+    # filled last prefix block for every writing sample but the last of each
+    # prompt, and each sample's own further blocks
+    copies = 0
+    if partial:
+        for g in range(prompts):
+            writers = int((suffix[g * samples:(g + 1) * samples] > 0).sum())
+            copies += max(writers - 1, 0)
+    needed = prompts * prefix_blocks + copies + sum(
+        max(_blocks(int(c)) - prefix_blocks, 0) for c in ctx)
     pool = math.ceil(1.1 * needed)
     order = np.random.Generator(np.random.PCG64(st[1])).permutation(pool)
     alloc = BlockAllocator(pool, BLOCK_SIZE, free_order=order)
@@ -225,11 +237,20 @@ def _shared_prefix(st) -> Workload:
             slots.append(slot)
             if pair is not None:
                 pairs.append(pair)
-    MB = _blocks(prefix + 256)
+    MB = _blocks(prefix + suffix_hi)
     group_start = np.arange(0, prompts * samples + 1, samples, dtype=np.int32)
     shared = np.full(prompts, full_prefix_blocks, dtype=np.int32)
-    return _finish(4, CONFIG_NAMES[4], "bf16", H, D, alloc, seqs, ctx, MB, st, len(slots),
+    return _finish(index, name, dtype, H, D, alloc, seqs, ctx, MB, st, len(slots),
                    slots, pairs, group_start=group_start, shared_blocks=shared)
+
+
+def make_shared_case(prompts, samples, prefix, suffix_lo, suffix_hi, num_heads, head_dim,
+                     dtype="f16", seed=0) -> Workload:
+    """A shared-prefix decode step (the recipe of the parallel-sampling
+    workload) with free sizes, for edge-case tests."""
+    st = np.random.SeedSequence(seed).spawn(8)
+    return _shared_prefix(st, 0, "custom_shared", prompts, samples, prefix, suffix_lo, suffix_hi,
+                          num_heads, head_dim, dtype)
 
 
 def poison_unused(w: Workload) -> Workload:
