@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention KV GB/s + seqs/s, % of MI355X HBM peak (LLaMA-7B shape)"
 DECODE_SOURCES = ["paged_kv_cache_159_amd/csrc/pkv_decode.hip",
+                  "paged_kv_cache_159_amd/csrc/pkv_partition.h",
                   "paged_kv_cache_159_amd/csrc/pkv_device.h"]
 
 

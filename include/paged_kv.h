@@ -143,7 +143,7 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens,
 
 /*
  * Workspace bytes paged_attention_decode_grouped needs: fp32 partials of every
- * shared-prefix chunk (4 blocks) and every tail partition of every (sequence,
+ * shared-prefix chunk (8 blocks) and every tail partition of every (sequence,
  * head). Returns 0 when the arguments are invalid.
  */
 size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int head_dim,
@@ -166,7 +166,8 @@ size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int h
  *                  (shared_blocks[g] * block_size <= context_lens[s]).
  * Groups of any size are allowed (queries are processed 16 at a time); a
  * group with shared_blocks 0, or of one sequence, takes the ordinary path.
- * Three launches on `stream`: shared-prefix chunks, tail partitions, merge.
+ * Two launches on `stream`: shared-prefix chunks and tail partitions in one
+ * grid, then the merge.
  * `workspace` needs paged_attention_grouped_workspace_size(...) bytes.
  */
 int paged_attention_decode_grouped(void* out, const void* query,

@@ -115,7 +115,9 @@ int check_grouped(int num_seqs, int num_heads, int head_dim, int block_size,
   grouped_slots(max_blocks_per_seq, block_size, chunk_slots, tail_parts);
   const int64_t slots = (int64_t)*chunk_slots + *tail_parts;
   if ((int64_t)num_seqs * num_heads * slots > kMaxGrid) return PKV_ERR_SHAPE;
-  if ((int64_t)num_groups * (*chunk_slots) * num_heads > kMaxGrid) return PKV_ERR_SHAPE;
+  if ((int64_t)num_groups * (*chunk_slots) * num_heads + (int64_t)num_seqs * num_heads * slots >
+      kMaxGrid)
+    return PKV_ERR_SHAPE;
   *need = pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)slots);
   return PKV_OK;
 }
@@ -268,9 +270,7 @@ int paged_attention_decode_grouped(void* out, const void* query, const void* key
   a.dtype = dtype;
   pkv::decode_workspace_split(workspace, num_seqs, num_heads, a.num_parts, &a.ws_ml, &a.ws_o);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = status_of(pkv::launch_decode_shared(a, st));
-  if (rc) return rc;
-  rc = status_of(pkv::launch_decode_partitions(a, st));
+  rc = status_of(pkv::launch_decode_grouped(a, st));
   if (rc) return rc;
   return status_of(pkv::launch_decode_merge(a, st));
 }

@@ -37,16 +37,10 @@
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_partition.h"
 
 namespace pkv {
 
-constexpr int kWaves = 8;
-constexpr int kRowsPerWave = kBlockSize / kWaves;  // rows of a block each wave reads
-
-// TAIL = true is the grouped call's second launch: each sequence starts after
-// its group's shared blocks (those are handled by the shared-prefix kernel),
-// its partitions go to partial slots slot_base + p, and every partition
-// writes a partial (the merge always runs).
 template <typename T, int D, int PT, bool TAIL>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
@@ -59,138 +53,11 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         const int32_t* __restrict__ group_start,
                         const int32_t* __restrict__ shared_blocks, int num_groups,
                         int slot_base) {
-  using E = Elem<T>;
-  constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
-  constexpr int HG = 64 / LPR;       // heads per wave-wide load
-  static_assert(PT % kBlockSize == 0, "partition is whole blocks");
-
-  const int H = num_heads;
-  const int groups = (H + HG - 1) / HG;
-  const int g = blockIdx.x % groups;
-  const int sp = blockIdx.x / groups;
-  const int s = sp % num_seqs;
-  const int p = sp / num_seqs;
-  const int ctx = context_lens[s];
-  int tok0 = 0;   // first token this launch covers for sequence s
-  if constexpr (TAIL) tok0 = shared_blocks[group_of(s, group_start, num_groups)] * kBlockSize;
-  const int tok_begin = tok0 + p * PT;
-  if (tok_begin >= ctx) return;
-  const int tok_end = min(ctx, tok_begin + PT);
-  const int blk_begin = tok_begin / kBlockSize;
-  const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int hl = lane / LPR;          // head within the group
-  const int c = lane % LPR;           // 8-element column chunk
-  const int h = g * HG + hl;
-  const bool head_ok = h < H;
-  const int hr = head_ok ? h : 0;     // lanes past the last head read head 0 and are ignored
-
-  const uint4 qv = *reinterpret_cast<const uint4*>(query + ((size_t)s * H + hr) * D + c * 8);
-  const int32_t* bt = block_tables + (size_t)s * max_blocks + blk_begin;
-  const uint32_t kv_dim = (uint32_t)H * D;
-  const size_t blk_bytes = (size_t)kBlockSize * kv_dim * sizeof(uint16_t);
-  const uint32_t col_bytes = ((uint32_t)hr * D + (uint32_t)c * 8) * sizeof(uint16_t);
-  const char* kpool = reinterpret_cast<const char*>(key_cache);
-  const char* vpool = reinterpret_cast<const char*>(value_cache);
-
-  float m = -INFINITY, l = 0.f;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-
-  for (int b = 0; b < nblk; ++b) {
-    const int phys = bt[b];
-    const int rows = min(kBlockSize, ctx - (blk_begin + b) * kBlockSize);
-    const char* kb = kpool + (size_t)phys * blk_bytes;
-    const char* vb = vpool + (size_t)phys * blk_bytes;
-    // Rows past the context re-read row 0 of the block (a valid token, a
-    // cache hit) instead of branching; their weight is exactly 0 below.
-    uint4 kr[kRowsPerWave], vr[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int row = wave + i * kWaves;
-      const uint32_t rr = row < rows ? (uint32_t)row : 0u;
-      const uint32_t off = rr * kv_dim * (uint32_t)sizeof(uint16_t) + col_bytes;
-      kr[i] = *reinterpret_cast<const uint4*>(kb + off);
-      vr[i] = *reinterpret_cast<const uint4*>(vb + off);
-    }
-    float sc[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      float d = E::dot2(kr[i].x, qv.x, 0.f);
-      d = E::dot2(kr[i].y, qv.y, d);
-      d = E::dot2(kr[i].z, qv.z, d);
-      d = E::dot2(kr[i].w, qv.w, d);
-      d = group_sum<LPR>(d);
-      sc[i] = (wave + i * kWaves < rows) ? d * scale_log2 : -INFINITY;
-    }
-    float bm = sc[0];
-#pragma unroll
-    for (int i = 1; i < kRowsPerWave; ++i) bm = fmaxf(bm, sc[i]);
-    const float mn = fmaxf(m, bm);
-    // While a stream has seen no valid row, m and mn are -inf; using 0 as the
-    // reference then makes every weight 2^-inf = 0 without a branch (a
-    // divergent branch here would make the compiler wait for all loads).
-    const float ref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - ref);
-    l *= alpha;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const float pw = fast_exp2(sc[i] - ref);
-      l += pw;
-      acc[0] += pw * E::lo(vr[i].x);
-      acc[1] += pw * E::hi(vr[i].x);
-      acc[2] += pw * E::lo(vr[i].y);
-      acc[3] += pw * E::hi(vr[i].y);
-      acc[4] += pw * E::lo(vr[i].z);
-      acc[5] += pw * E::hi(vr[i].z);
-      acc[6] += pw * E::lo(vr[i].w);
-      acc[7] += pw * E::hi(vr[i].w);
-    }
-    m = mn;
-  }
-
-  // Merge the waves' streams of each head through LDS.
-  __shared__ float s_m[kWaves][HG], s_l[kWaves][HG];
-  __shared__ float s_acc[kWaves][HG * D];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) s_acc[wave][hl * D + c * 8 + j] = acc[j];
-  if (c == 0) {
-    s_m[wave][hl] = m;
-    s_l[wave][hl] = l;
-  }
-  __syncthreads();
-  const int parts_s = TAIL ? 0 : (ctx + PT - 1) / PT;
-  for (int o = threadIdx.x; o < HG * D; o += kWaves * 64) {
-    const int ol = o / D;
-    const int d = o % D;
-    const int oh = g * HG + ol;
-    if (oh >= H) break;   // o grows, so later o are past H too
-    float M = s_m[0][ol];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][ol]);
-    float L = 0.f, val = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float cw = (s_m[w][ol] == -INFINITY) ? 0.f : fast_exp2(s_m[w][ol] - M);
-      L += s_l[w][ol] * cw;
-      val += s_acc[w][o] * cw;
-    }
-    if (parts_s == 1) {
-      out[((size_t)s * H + oh) * D + d] = E::round(val / L);
-    } else {
-      const size_t pi = ((size_t)s * H + oh) * num_parts + slot_base + p;
-      ws_o[pi * D + d] = val / L;
-      if (d == 0) {
-        ws_ml[pi * 2] = M;
-        ws_ml[pi * 2 + 1] = L;
-      }
-    }
-  }
+  __shared__ __align__(16) uint8_t lds[partition_lds_bytes<D>()];
+  partition_body<T, D, PT, TAIL>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
+                                 block_tables, context_lens, num_seqs, num_heads, max_blocks,
+                                 num_parts, scale_log2, group_start, shared_blocks, num_groups,
+                                 slot_base, lds);
 }
 
 // Log-sum-exp merge of the partials of one (sequence, head). Partials live in
@@ -198,8 +65,8 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
 // (the plain call uses only the first range; the grouped call puts the
 // shared-prefix chunks in the first and the tail partitions in the second).
 // 256 threads: thread (k, d) sums slots k, k + K, ... for output element d
-// (K = 256 / D), then the K partial sums meet in LDS. The loads of different
-// slots are independent, so many are in flight.
+// (K = 256 / D), then the K partial sums meet in LDS (one barrier). The loads
+// of different slots are independent, so many are in flight.
 constexpr int kMergeThreads = 256;
 
 template <typename T, int D, bool GROUPED>
@@ -231,19 +98,12 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
   const size_t base = ((size_t)s * H + h) * num_parts;
   const int d = threadIdx.x % D;
   const int k = threadIdx.x / D;
-  __shared__ float s_red[kMergeThreads];
+  // The maximum over all partials: the addresses are the same in every
+  // thread, so these are scalar loads and need no cross-thread reduction.
   float M = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += kMergeThreads) M = fmaxf(M, ws_ml[(base + slot(i)) * 2]);
-  s_red[threadIdx.x] = M;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) s_red[threadIdx.x] = fmaxf(s_red[threadIdx.x], s_red[threadIdx.x + w]);
-    __syncthreads();
-  }
-  M = s_red[0];
-  __syncthreads();
+  for (int i = 0; i < n; ++i) M = fmaxf(M, ws_ml[(base + slot(i)) * 2]);
   float L = 0.f, o = 0.f;
-#pragma unroll 4
+#pragma unroll 8
   for (int i = k; i < n; i += K) {
     const size_t pi = base + slot(i);
     const float cw = ws_ml[pi * 2 + 1] * fast_exp2(ws_ml[pi * 2] - M);

@@ -12,7 +12,7 @@ namespace pkv {
 constexpr int kCopyVecsPerGroup = 1024;
 
 // Grouped decode: shared-prefix blocks per workgroup of the shared-prefix kernel.
-constexpr int kSharedChunkBlocks = 4;
+constexpr int kSharedChunkBlocks = 8;
 
 struct DecodeArgs {
   void* out;
@@ -48,8 +48,9 @@ void decode_workspace_split(void* ws, int num_seqs, int num_heads, int num_parts
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
-// Grouped call, first launch: the shared-prefix blocks of every group.
-hipError_t launch_decode_shared(const DecodeArgs& a, hipStream_t stream);
+// Grouped call, main launch: shared-prefix units and tail partitions in one
+// grid (the merge follows with launch_decode_merge).
+hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int64_t* slot_mapping, int num_tokens,

@@ -1,0 +1,169 @@
+// Body of the decode partition kernel, shared by the plain decode launch and
+// the grouped decode launch (whose tail partitions run the same code).
+#pragma once
+
+#include "pkv_device.h"
+
+namespace pkv {
+
+constexpr int kWaves = 8;
+constexpr int kRowsPerWave = kBlockSize / kWaves;  // rows of a block each wave reads
+
+// LDS bytes partition_body needs: per wave and head (max, sum), and per wave a
+// head group's accumulators.
+template <int D>
+constexpr int partition_lds_bytes() {
+  constexpr int HG = 64 / (D / 8);
+  return (2 * kWaves * HG + kWaves * HG * D) * (int)sizeof(float);
+}
+
+// One workgroup (index wg) of the partition launch: (head group, sequence,
+// partition), head groups fastest. TAIL = true is the grouped call's tail:
+// each sequence starts after its group's shared blocks (handled by the
+// shared-prefix units), its partitions go to partial slots slot_base + p, and
+// every partition writes a partial (the merge always runs).
+template <typename T, int D, int PT, bool TAIL>
+__device__ __forceinline__ void partition_body(
+    int wg, uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
+    const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int num_seqs, int num_heads, int max_blocks,
+    int num_parts, float scale_log2, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ shared_blocks, int num_groups, int slot_base, uint8_t* lds) {
+  using E = Elem<T>;
+  constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
+  constexpr int HG = 64 / LPR;       // heads per wave-wide load
+  static_assert(PT % kBlockSize == 0, "partition is whole blocks");
+
+  const int H = num_heads;
+  const int groups = (H + HG - 1) / HG;
+  const int g = wg % groups;
+  const int sp = wg / groups;
+  const int s = sp % num_seqs;
+  const int p = sp / num_seqs;
+  const int ctx = context_lens[s];
+  int tok0 = 0;   // first token this launch covers for sequence s
+  if constexpr (TAIL) tok0 = shared_blocks[group_of(s, group_start, num_groups)] * kBlockSize;
+  const int tok_begin = tok0 + p * PT;
+  if (tok_begin >= ctx) return;
+  const int tok_end = min(ctx, tok_begin + PT);
+  const int blk_begin = tok_begin / kBlockSize;
+  const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hl = lane / LPR;          // head within the group
+  const int c = lane % LPR;           // 8-element column chunk
+  const int h = g * HG + hl;
+  const bool head_ok = h < H;
+  const int hr = head_ok ? h : 0;     // lanes past the last head read head 0 and are ignored
+
+  const uint4 qv = *reinterpret_cast<const uint4*>(query + ((size_t)s * H + hr) * D + c * 8);
+  const int32_t* bt = block_tables + (size_t)s * max_blocks + blk_begin;
+  const uint32_t kv_dim = (uint32_t)H * D;
+  const size_t blk_bytes = (size_t)kBlockSize * kv_dim * sizeof(uint16_t);
+  const uint32_t col_bytes = ((uint32_t)hr * D + (uint32_t)c * 8) * sizeof(uint16_t);
+  const char* kpool = reinterpret_cast<const char*>(key_cache);
+  const char* vpool = reinterpret_cast<const char*>(value_cache);
+
+  float m = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+
+  for (int b = 0; b < nblk; ++b) {
+    const int phys = bt[b];
+    const int rows = min(kBlockSize, ctx - (blk_begin + b) * kBlockSize);
+    const char* kb = kpool + (size_t)phys * blk_bytes;
+    const char* vb = vpool + (size_t)phys * blk_bytes;
+    // Rows past the context re-read row 0 of the block (a valid token, a
+    // cache hit) instead of branching; their weight is exactly 0 below.
+    uint4 kr[kRowsPerWave], vr[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int row = wave + i * kWaves;
+      const uint32_t rr = row < rows ? (uint32_t)row : 0u;
+      const uint32_t off = rr * kv_dim * (uint32_t)sizeof(uint16_t) + col_bytes;
+      kr[i] = *reinterpret_cast<const uint4*>(kb + off);
+      vr[i] = *reinterpret_cast<const uint4*>(vb + off);
+    }
+    float sc[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      float d = E::dot2(kr[i].x, qv.x, 0.f);
+      d = E::dot2(kr[i].y, qv.y, d);
+      d = E::dot2(kr[i].z, qv.z, d);
+      d = E::dot2(kr[i].w, qv.w, d);
+      d = group_sum<LPR>(d);
+      sc[i] = (wave + i * kWaves < rows) ? d * scale_log2 : -INFINITY;
+    }
+    float bm = sc[0];
+#pragma unroll
+    for (int i = 1; i < kRowsPerWave; ++i) bm = fmaxf(bm, sc[i]);
+    const float mn = fmaxf(m, bm);
+    // While a stream has seen no valid row, m and mn are -inf; using 0 as the
+    // reference then makes every weight 2^-inf = 0 without a branch (a
+    // divergent branch here would make the compiler wait for all loads).
+    const float ref = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m - ref);
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const float pw = fast_exp2(sc[i] - ref);
+      l += pw;
+      acc[0] += pw * E::lo(vr[i].x);
+      acc[1] += pw * E::hi(vr[i].x);
+      acc[2] += pw * E::lo(vr[i].y);
+      acc[3] += pw * E::hi(vr[i].y);
+      acc[4] += pw * E::lo(vr[i].z);
+      acc[5] += pw * E::hi(vr[i].z);
+      acc[6] += pw * E::lo(vr[i].w);
+      acc[7] += pw * E::hi(vr[i].w);
+    }
+    m = mn;
+  }
+
+  // Merge the waves' streams of each head through LDS.
+  float(*s_m)[HG] = reinterpret_cast<float(*)[HG]>(lds);
+  float(*s_l)[HG] = reinterpret_cast<float(*)[HG]>(lds + kWaves * HG * sizeof(float));
+  float(*s_acc)[HG * D] =
+      reinterpret_cast<float(*)[HG * D]>(lds + 2 * kWaves * HG * sizeof(float));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s_acc[wave][hl * D + c * 8 + j] = acc[j];
+  if (c == 0) {
+    s_m[wave][hl] = m;
+    s_l[wave][hl] = l;
+  }
+  __syncthreads();
+  const int parts_s = TAIL ? 0 : (ctx + PT - 1) / PT;
+  for (int o = threadIdx.x; o < HG * D; o += kWaves * 64) {
+    const int ol = o / D;
+    const int d = o % D;
+    const int oh = g * HG + ol;
+    if (oh >= H) break;   // o grows, so later o are past H too
+    float M = s_m[0][ol];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][ol]);
+    float L = 0.f, val = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float cw = (s_m[w][ol] == -INFINITY) ? 0.f : fast_exp2(s_m[w][ol] - M);
+      L += s_l[w][ol] * cw;
+      val += s_acc[w][o] * cw;
+    }
+    if (parts_s == 1) {
+      out[((size_t)s * H + oh) * D + d] = E::round(val / L);
+    } else {
+      const size_t pi = ((size_t)s * H + oh) * num_parts + slot_base + p;
+      ws_o[pi * D + d] = val / L;
+      if (d == 0) {
+        ws_ml[pi * 2] = M;
+        ws_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace pkv
