@@ -33,8 +33,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention KV GB/s + seqs/s, % of MI355X HBM peak (LLaMA-7B shape)"
 DECODE_SOURCES = ["paged_kv_cache_159_amd/csrc/pkv_decode.hip",
+                  "paged_kv_cache_159_amd/csrc/pkv_grouped.hip",
                   "paged_kv_cache_159_amd/csrc/pkv_partition.h",
+                  "paged_kv_cache_159_amd/csrc/pkv_launch.h",
                   "paged_kv_cache_159_amd/csrc/pkv_device.h"]
+# Kernels whose dispatches make up one timed decode launch, per mode.
+TIMED_KERNELS = {"plain": ("decode_partition_kernel",),
+                 "grouped": ("decode_grouped_kernel", "decode_merge_kernel")}
 
 
 def parse():
@@ -49,6 +54,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ungrouped", action="store_true",
                     help="shared-prefix workload: use the plain decode instead of the grouped one")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="turn rocprofv3 counter_collection.csv files (FETCH_SIZE and WRITE_SIZE "
+                         "runs of this bench, then of --calibrate-copy) into "
+                         "profiles/traffic_<workload>.json and .md, and exit (no GPU needed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -109,10 +119,105 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name):
+def traffic_key(w, grouped):
+    return w.name + ("_grouped" if grouped else "")
+
+
+def _counter_per_dispatch(path):
+    """{dispatch id: (kernel name, summed counter value in KiB)} of one
+    rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            d = int(row["Dispatch_Id"])
+            short = row["Kernel_Name"].split("(")[0].replace("void ", "")
+            name, v = out.get(d, (short, 0.0))
+            out[d] = (name, v + float(row["Counter_Value"]))
+    return out
+
+
+def traffic_summary(paths, w, grouped):
+    """HBM bytes per timed decode launch from FETCH_SIZE / WRITE_SIZE counters,
+    each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    fetch, write, cal_f, cal_w = (_counter_per_dispatch(p) for p in paths)
+    kib = float(1 << 20)                         # 1 GiB in KiB
+
+    def copy_value(c):
+        vals = sorted(v for n, v in c.values() if "copy" in n.lower())
+        if not vals:
+            raise SystemExit("no copy kernel in the calibration counters")
+        return float(np.median(vals[-5:]))       # the five 1 GiB copies are the largest
+
+    cf, cw = copy_value(cal_f), copy_value(cal_w)
+    ff, fw = kib / cf, kib / cw
+    names = TIMED_KERNELS["grouped" if grouped else "plain"]
+
+    def per_launch(c):
+        per_kernel = {}
+        for n, v in c.values():
+            for k in names:
+                if k in n:
+                    per_kernel.setdefault(n, []).append(v)
+        if not per_kernel:
+            raise SystemExit(f"no {names} dispatch in the counters")
+        return {n: float(np.mean(v)) for n, v in per_kernel.items()}, \
+            {n: len(v) for n, v in per_kernel.items()}
+
+    fk, nf = per_launch(fetch)
+    wk, _ = per_launch(write)
+    fetch_b = sum(fk.values()) * 1024 * ff
+    write_b = sum(wk.values()) * 1024 * fw
+    dec_b = algorithmic_bytes(w)[0]
+    res = {
+        "kernels": sorted(fk),
+        "workload": f"{w.name} ({w.num_seqs} seqs x {w.num_heads} heads x {w.head_dim}, {w.dtype}, "
+                    f"bs {w.block_size}, sum ctx {w.total_context})",
+        "mode": "grouped" if grouped else "plain",
+        "decode_source_digest": source_digest(),
+        "fetch_size_kib_per_dispatch": {n: round(v, 1) for n, v in fk.items()},
+        "write_size_kib_per_dispatch": {n: round(v, 1) for n, v in wk.items()},
+        "dispatches": nf,
+        "calibration": {"reference": "plain 1 GiB device copy (bench.py --calibrate-copy)",
+                        "fetch_size_kib": round(cf, 1), "write_size_kib": round(cw, 1),
+                        "fetch_factor": round(ff, 5), "write_factor": round(fw, 5)},
+        "bytes_per_launch": int(round(fetch_b + write_b)),
+        "fetch_bytes_per_launch": int(round(fetch_b)),
+        "write_bytes_per_launch": int(round(write_b)),
+        "algorithmic_bytes_per_launch": int(dec_b),
+        "fetch_over_algorithmic": round(fetch_b / dec_b, 4),
+        "counter_files": [os.path.relpath(p, ROOT) for p in paths],
+    }
+    key = traffic_key(w, grouped)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    lines = [f"# HBM traffic of the timed decode launch ({key})", "",
+             "rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, one counter per run, "
+             "then the same two counters over `bench.py --calibrate-copy` (five 1 GiB "
+             "device copies). Written by `python bench.py --workload "
+             f"{w.index}{' --ungrouped' if (w.group_start is not None and not grouped) else ''} "
+             "--traffic-summary <fetch csv> <write csv> <cal fetch csv> <cal write csv>`.", "",
+             "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches |",
+             "|---|---|---|---|"]
+    for n in sorted(fk):
+        lines.append(f"| {n} | {fk[n]:,.1f} | {wk.get(n, float('nan')):,.1f} | {nf[n]} |")
+    lines += ["", f"Calibration: the 1 GiB copy reads FETCH_SIZE {cf:,.1f} KiB and WRITE_SIZE "
+              f"{cw:,.1f} KiB per dispatch, so the factors are {ff:.4f} (fetch) and {fw:.4f} "
+              "(write).", "",
+              f"Per launch: fetched {fetch_b / 1e9:.4f} GB, written {write_b / 1e6:.2f} MB; "
+              f"algorithmic bytes {dec_b / 1e9:.4f} GB; fetch / algorithmic = "
+              f"{fetch_b / dec_b:.4f}.", "", "Kernel source digest: "
+              f"`{res['decode_source_digest']}`.", ""]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{key}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(res, indent=1))
+
+
+def load_traffic(key):
     """HBM traffic per decode launch from committed rocprofv3 counter runs,
     only if they were taken on the current decode kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -168,6 +273,12 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.traffic_summary:
+        sys.path.insert(0, ROOT)
+        from workloads import make_config
+        w = make_config(args.workload)
+        traffic_summary(args.traffic_summary, w, w.group_start is not None and not args.ungrouped)
         return
 
     import torch
@@ -256,7 +367,7 @@ def main():
           f"(p10 {np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f}) -> "
           f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak", file=sys.stderr, flush=True)
 
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(traffic_key(w, grouped))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
