@@ -208,7 +208,19 @@ def traffic_summary(paths, w, grouped):
               f"Per launch: fetched {fetch_b / 1e9:.4f} GB, written {write_b / 1e6:.2f} MB; "
               f"algorithmic bytes {dec_b / 1e9:.4f} GB; fetch / algorithmic = "
               f"{fetch_b / dec_b:.4f}.", "", "Kernel source digest: "
-              f"`{res['decode_source_digest']}`.", ""]
+              f"`{res['decode_source_digest']}`.", "", "Counter runs (repo root, MI355X):", ""]
+    ung = " --ungrouped" if (w.group_start is not None and not grouped) else ""
+    for ctr, path, prog in (("FETCH_SIZE", paths[0], f"--steps 10 --warmup 2 --no-cpu-baseline "
+                                                     f"--workload {w.index}{ung}"),
+                            ("WRITE_SIZE", paths[1], f"--steps 10 --warmup 2 --no-cpu-baseline "
+                                                     f"--workload {w.index}{ung}"),
+                            ("FETCH_SIZE", paths[2], "--calibrate-copy"),
+                            ("WRITE_SIZE", paths[3], "--calibrate-copy")):
+        d = os.path.relpath(os.path.dirname(path), ROOT)
+        o = os.path.basename(path).split("_counter_collection")[0]
+        lines += ["```", f"rocprofv3 --pmc {ctr} --kernel-trace --output-format csv -d {d} -o {o} "
+                  f"-- python -u bench.py {prog}", "```"]
+    lines.append("")
     with open(os.path.join(ROOT, "profiles", f"traffic_{key}.md"), "w") as f:
         f.write("\n".join(lines))
     print(json.dumps(res, indent=1))
