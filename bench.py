@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, help="workload index 1..5 (default 2)")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="tokens per KV block (default 16; 8 and 32 rebuild the same "
+                         "workload's pools and tables at that size)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline sample")
@@ -120,7 +123,8 @@ def source_digest():
 
 
 def traffic_key(w, grouped):
-    return w.name + ("_grouped" if grouped else "")
+    return (w.name + ("" if w.block_size == 16 else f"_bs{w.block_size}") +
+            ("_grouped" if grouped else ""))
 
 
 def _counter_per_dispatch(path):
@@ -196,7 +200,8 @@ def traffic_summary(paths, w, grouped):
              "rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE`, one counter per run, "
              "then the same two counters over `bench.py --calibrate-copy` (five 1 GiB "
              "device copies). Written by `python bench.py --workload "
-             f"{w.index}{' --ungrouped' if (w.group_start is not None and not grouped) else ''} "
+             f"{w.index}{' --ungrouped' if (w.group_start is not None and not grouped) else ''}"
+             f"{'' if w.block_size == 16 else f' --block-size {w.block_size}'} "
              "--traffic-summary <fetch csv> <write csv> <cal fetch csv> <cal write csv>`.", "",
              "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches |",
              "|---|---|---|---|"]
@@ -210,6 +215,8 @@ def traffic_summary(paths, w, grouped):
               f"{fetch_b / dec_b:.4f}.", "", "Kernel source digest: "
               f"`{res['decode_source_digest']}`.", "", "Counter runs (repo root, MI355X):", ""]
     ung = " --ungrouped" if (w.group_start is not None and not grouped) else ""
+    if w.block_size != 16:
+        ung += f" --block-size {w.block_size}"
     for ctr, path, prog in (("FETCH_SIZE", paths[0], f"--steps 10 --warmup 2 --no-cpu-baseline "
                                                      f"--workload {w.index}{ung}"),
                             ("WRITE_SIZE", paths[1], f"--steps 10 --warmup 2 --no-cpu-baseline "
@@ -289,7 +296,7 @@ def main():
     if args.traffic_summary:
         sys.path.insert(0, ROOT)
         from workloads import make_config
-        w = make_config(args.workload)
+        w = make_config(args.workload, args.block_size)
         traffic_summary(args.traffic_summary, w, w.group_start is not None and not args.ungrouped)
         return
 
@@ -306,7 +313,7 @@ def main():
     pkv.lib()
 
     t0 = time.time()
-    w = make_config(args.workload)
+    w = make_config(args.workload, args.block_size)
     print(f"[bench] workload {w.index} {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} "
           f"{w.dtype} NB={w.num_blocks} sum(ctx)={w.total_context} generated in {time.time() - t0:.1f} s",
           file=sys.stderr, flush=True)
@@ -316,7 +323,8 @@ def main():
     R = min(R, 16)
     kcs = [dw.key_cache] + [dw.key_cache.clone() for _ in range(R - 1)]
     vcs = [dw.value_cache] + [dw.value_cache.clone() for _ in range(R - 1)]
-    ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq, device=dev)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                             w.block_size, device=dev)
     outs = [torch.empty_like(dw.query) for _ in range(R)]
     dec_b, write_b, copy_b, logical_b = algorithmic_bytes(w)
     step_bytes = dec_b + write_b + copy_b
@@ -330,7 +338,7 @@ def main():
         gs = torch.from_numpy(w.group_start).to(dev)
         sb = torch.from_numpy(w.shared_blocks).to(dev)
         gws = torch.empty(max(pkv.grouped_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
-                                                         w.max_blocks_per_seq), 16),
+                                                         w.max_blocks_per_seq, w.block_size), 16),
                           dtype=torch.uint8, device=dev)
 
     def step(i, record):
@@ -356,7 +364,8 @@ def main():
         if record:
             e1.record()
             ev.append((e0, e1))
-        pkv.paged_attention_decode_merge(outs[r], dw.context_lens, w.max_blocks_per_seq, ws)
+        pkv.paged_attention_decode_merge(outs[r], dw.context_lens, w.max_blocks_per_seq, ws,
+                                         block_size=w.block_size)
 
     for i in range(args.warmup):
         step(i, False)

@@ -30,8 +30,12 @@
  *   slot_mapping            int64 [num_tokens]; slot = physical*block_size + offset
  *   block_mapping           int32 [num_pairs][2] = (src, dst)
  *
- * Supported now: block_size 16 (the pages' default: P2 "KV Cache逻辑块物理块映射
- * 机制"; P4 "块大小"), head_dim 64 or 128, any num_heads >= 1.
+ * Supported: block_size 8, 16 or 32 (16 is the pages' default; larger blocks
+ * mean fewer table entries and lookups, smaller ones less waste in a
+ * sequence's last block: P2 "KV Cache逻辑块物理块映射机制" and "vLLM高性能推理
+ * 架构的工程落地考量"; P4 "PagedAttention: 页式管理内存"; P1 §3.3.5
+ * "自动调优策略"), head_dim 64 or 128, any num_heads >= 1. Any other block
+ * size or head_dim returns PKV_ERR_UNSUPPORTED.
  *
  * Ownership: the caller owns every buffer (pools, query, out, tables,
  * workspace). The library allocates and frees nothing and keeps no state
@@ -143,8 +147,8 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens,
 
 /*
  * Workspace bytes paged_attention_decode_grouped needs: fp32 partials of every
- * shared-prefix chunk (8 blocks) and every tail partition of every (sequence,
- * head). Returns 0 when the arguments are invalid.
+ * shared-prefix chunk (128 tokens) and every tail partition of every
+ * (sequence, head). Returns 0 when the arguments are invalid.
  */
 size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int head_dim,
                                               int max_blocks_per_seq, int block_size);
@@ -164,8 +168,10 @@ size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int h
  *                  block-table entries are identical for every member of
  *                  group g and are full blocks of every member's context
  *                  (shared_blocks[g] * block_size <= context_lens[s]).
- * Groups of any size are allowed (queries are processed 16 at a time); a
- * group with shared_blocks 0, or of one sequence, takes the ordinary path.
+ * Groups of any size are allowed (queries are processed 16 at a time). The
+ * MFMA units cover the shared tokens rounded down to a multiple of 16 (at
+ * block_size 8 an odd last shared block goes with the tails); a group with
+ * shared_blocks 0 runs entirely on the tail partitions.
  * Two launches on `stream`: shared-prefix chunks and tail partitions in one
  * grid, then the merge.
  * `workspace` needs paged_attention_grouped_workspace_size(...) bytes.

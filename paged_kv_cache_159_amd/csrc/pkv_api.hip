@@ -21,7 +21,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Checks common to every call: element type, block size, head geometry, pool.
 int check_layout(int dtype, int block_size, int num_heads, int head_dim, int num_blocks) {
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (block_size != pkv::kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (!pkv::supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (num_heads < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
   // in-block element offsets are 32-bit
@@ -85,6 +85,7 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->num_heads = num_heads;
   a->head_dim = head_dim;
   a->max_blocks_per_seq = max_blocks_per_seq;
+  a->block_size = block_size;
   a->num_parts = parts;
   a->part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
   a->scale = scale;
@@ -102,7 +103,9 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
 
 // Partial slots of the grouped call: shared-prefix chunks, then tail partitions.
 void grouped_slots(int max_blocks_per_seq, int block_size, int* chunk_slots, int* tail_parts) {
-  *chunk_slots = (max_blocks_per_seq + pkv::kSharedChunkBlocks - 1) / pkv::kSharedChunkBlocks;
+  // shared tokens <= max_blocks_per_seq * block_size, in chunks of 8 tiles of 16
+  constexpr int64_t chunk_tokens = pkv::kSharedChunkTiles * pkv::kTileTokens;
+  *chunk_slots = (int)(((int64_t)max_blocks_per_seq * block_size + chunk_tokens - 1) / chunk_tokens);
   *tail_parts = num_partitions(max_blocks_per_seq, block_size);
 }
 
@@ -188,6 +191,7 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens, int num
   a.num_heads = num_heads;
   a.head_dim = head_dim;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_size;
   a.num_parts = parts;
   a.tail_parts = parts;
   a.part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
@@ -259,6 +263,7 @@ int paged_attention_decode_grouped(void* out, const void* query, const void* key
   a.num_heads = num_heads;
   a.head_dim = head_dim;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_size;
   a.part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
   a.num_parts = chunk_slots + tail_parts;
   a.tail_parts = tail_parts;

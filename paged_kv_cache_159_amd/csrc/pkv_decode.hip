@@ -1,6 +1,6 @@
 // Paged decode attention for gfx950: one query per (sequence, head) attends
-// over that sequence's tokens, which live in 16-token physical blocks reached
-// through the sequence's block table.
+// over that sequence's tokens, which live in physical blocks of 16 tokens (or
+// 8 or 32) reached through the sequence's block table.
 //
 // Pages: [P3] "3.1 PagedAttention的核心原理" §3.1.3 (logical block = t / 16,
 // offset = t % 16, physical = block_table[logical]; the flat table is indexed
@@ -8,14 +8,20 @@
 // organised by physical block so reads within a block coalesce); [P1] "3.3
 // 页面级显存管理" §3.3.1 "显存访问模式的优化" (16 consecutive tokens of a block
 // are contiguous; one sequence's blocks visited close together in time).
+// Block size: 16 is the default the pages settle on; larger blocks mean fewer
+// table entries and lookups, smaller ones less waste in each sequence's last
+// block ([P2] "KV Cache逻辑块物理块映射机制" and "vLLM高性能推理架构的工程落地考量";
+// [P4] "PagedAttention: 页式管理内存"; [P1] §3.3.5 "自动调优策略" item 4). The
+// kernels are built for 8, 16 and 32.
 //
 // Work decomposition. One workgroup (8 waves) per (sequence, context
 // partition of PT tokens, group of HG heads). With the pool laid out
 // [block][token][head][dim], one token row holds all heads side by side, so
 // a head group's slice of a row is contiguous: HG = 4 heads x 128 dims (8 x 64)
 // = 1 KB, exactly one wave-wide 16-byte load. Lane (hl, c) holds 8 elements
-// of head hl. Wave w reads rows w and w+8 of every block of the partition, so
-// the 8 waves read the 16 rows of a block side by side. A block's physical id
+// of head hl. Wave w reads rows w, w+8, ... of every block of the partition
+// (1, 2 or 4 rows at block size 8, 16, 32), so the 8 waves read a block's
+// rows side by side. A block's physical id
 // is a wave-uniform scalar load; row addresses are that block base plus a
 // 32-bit lane offset. Workgroup ids run head groups fastest, so neighbouring
 // workgroups read neighbouring pieces of the same token rows.
@@ -41,7 +47,7 @@
 
 namespace pkv {
 
-template <typename T, int D, int PT, bool TAIL>
+template <typename T, int D, int PT, int BS, bool TAIL>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         float* __restrict__ ws_o, const uint16_t* __restrict__ query,
@@ -54,7 +60,7 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         const int32_t* __restrict__ shared_blocks, int num_groups,
                         int slot_base) {
   __shared__ __align__(16) uint8_t lds[partition_lds_bytes<D>()];
-  partition_body<T, D, PT, TAIL>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
+  partition_body<T, D, PT, BS, TAIL>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
                                  block_tables, context_lens, num_seqs, num_heads, max_blocks,
                                  num_parts, scale_log2, group_start, shared_blocks, num_groups,
                                  slot_base, lds);
@@ -75,7 +81,7 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
                     const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens,
                     int num_heads, int num_parts, int part_tokens,
                     const int32_t* __restrict__ group_start,
-                    const int32_t* __restrict__ shared_blocks, int num_groups, int chunk_blocks,
+                    const int32_t* __restrict__ shared_blocks, int num_groups, int block_size,
                     int slot_base) {
   using E = Elem<T>;
   constexpr int K = kMergeThreads / D;
@@ -85,9 +91,11 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
   const int ctx = context_lens[s];
   int n0, n1;
   if constexpr (GROUPED) {
-    const int sb = shared_blocks[group_of(s, group_start, num_groups)];
-    n0 = (sb + chunk_blocks - 1) / chunk_blocks;
-    n1 = (ctx - sb * kBlockSize + part_tokens - 1) / part_tokens;
+    constexpr int chunk_tokens = kSharedChunkTiles * kTileTokens;
+    const int st = shared_prefix_tokens(shared_blocks[group_of(s, group_start, num_groups)],
+                                        block_size);
+    n0 = (st + chunk_tokens - 1) / chunk_tokens;
+    n1 = (ctx - st + part_tokens - 1) / part_tokens;
   } else {
     n0 = (ctx + part_tokens - 1) / part_tokens;
     n1 = 0;
@@ -149,12 +157,12 @@ void decode_workspace_split(void* ws, int num_seqs, int num_heads, int num_parts
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int D, int PT, bool TAIL>
+template <typename T, int D, int PT, int BS, bool TAIL>
 hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
   constexpr int HG = 64 / (D / 8);
   const unsigned groups = (unsigned)(a.num_heads + HG - 1) / HG;
   const unsigned grid = (unsigned)a.num_seqs * groups * (unsigned)a.tail_parts;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, PT, TAIL>), dim3(grid), dim3(kWaves * 64), 0, st,
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, PT, BS, TAIL>), dim3(grid), dim3(kWaves * 64), 0, st,
                      static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o,
                      static_cast<const uint16_t*>(a.query),
                      static_cast<const uint16_t*>(a.key_cache),
@@ -164,12 +172,21 @@ hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t partitions_d(const DecodeArgs& a, hipStream_t st) {
+template <typename T, int D, int BS>
+hipError_t partitions_b(const DecodeArgs& a, hipStream_t st) {
   const bool tail = a.group_start != nullptr;
   if (a.part_tokens == 256)
-    return tail ? partitions_t<T, D, 256, true>(a, st) : partitions_t<T, D, 256, false>(a, st);
-  return tail ? partitions_t<T, D, 512, true>(a, st) : partitions_t<T, D, 512, false>(a, st);
+    return tail ? partitions_t<T, D, 256, BS, true>(a, st)
+                : partitions_t<T, D, 256, BS, false>(a, st);
+  return tail ? partitions_t<T, D, 512, BS, true>(a, st)
+              : partitions_t<T, D, 512, BS, false>(a, st);
+}
+
+template <typename T, int D>
+hipError_t partitions_d(const DecodeArgs& a, hipStream_t st) {
+  if (a.block_size == 8) return partitions_b<T, D, 8>(a, st);
+  if (a.block_size == 32) return partitions_b<T, D, 32>(a, st);
+  return partitions_b<T, D, 16>(a, st);
 }
 
 template <typename T, int D>
@@ -179,12 +196,12 @@ hipError_t merge_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_merge_kernel<T, D, true>), dim3(grid), dim3(kMergeThreads), 0, st,
                        static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
                        a.num_parts, a.part_tokens, a.group_start, a.shared_blocks, a.num_groups,
-                       kSharedChunkBlocks, a.slot_base);
+                       a.block_size, a.slot_base);
   } else {
     hipLaunchKernelGGL((decode_merge_kernel<T, D, false>), dim3(grid), dim3(kMergeThreads), 0, st,
                        static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
                        a.num_parts, a.part_tokens, a.group_start, a.shared_blocks, a.num_groups,
-                       kSharedChunkBlocks, 0);
+                       a.block_size, 0);
   }
   return hipGetLastError();
 }

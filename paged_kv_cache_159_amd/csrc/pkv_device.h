@@ -8,7 +8,20 @@
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;
+// Tokens per block the kernels are built for (the pages' default of 16 and the
+// smaller and larger sizes they weigh against it).
+constexpr bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
+
+// Tokens per tile of the grouped path's MFMA contraction (M = 16).
+constexpr int kTileTokens = 16;
+
+// Shared-prefix tokens the grouped path's MFMA units cover for a group whose
+// first `shared_blocks` blocks are shared: the shared tokens rounded down to
+// whole 16-token tiles. The rest (an odd last block at block size 8) is read
+// with the sequence's own tail.
+__host__ __device__ __forceinline__ int shared_prefix_tokens(int shared_blocks, int block_size) {
+  return (shared_blocks * block_size) & ~(kTileTokens - 1);
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));

@@ -11,8 +11,9 @@ namespace pkv {
 // copy_blocks: 16-byte vectors one workgroup copies (256 threads x 4 = 16 KiB).
 constexpr int kCopyVecsPerGroup = 1024;
 
-// Grouped decode: shared-prefix blocks per workgroup of the shared-prefix kernel.
-constexpr int kSharedChunkBlocks = 8;
+// Grouped decode: 16-token tiles of the shared prefix per shared-prefix unit
+// (128 tokens).
+constexpr int kSharedChunkTiles = 8;
 
 struct DecodeArgs {
   void* out;
@@ -25,6 +26,7 @@ struct DecodeArgs {
   int num_heads;
   int head_dim;
   int max_blocks_per_seq;
+  int block_size;       // tokens per block: 8, 16 or 32
   int part_tokens;      // tokens per context partition (decode_partition_tokens)
   int num_parts;        // partial slots per (sequence, head) in the workspace layout
   int tail_parts;       // partitions per sequence the partition launch covers
@@ -38,7 +40,7 @@ struct DecodeArgs {
   float* ws_o;          // [num_seqs][num_heads][num_parts][head_dim] normalised partial outputs
 };
 
-// Tokens per context partition for these sizes (64 or 256).
+// Tokens per context partition for these sizes (256 or 512).
 int decode_partition_tokens(int max_blocks_per_seq, int block_size);
 
 // Workspace layout shared by the two decode launches.

@@ -7,7 +7,6 @@
 namespace pkv {
 
 constexpr int kWaves = 8;
-constexpr int kRowsPerWave = kBlockSize / kWaves;  // rows of a block each wave reads
 
 // LDS bytes partition_body needs: per wave and head (max, sum), and per wave a
 // head group's accumulators.
@@ -18,11 +17,15 @@ constexpr int partition_lds_bytes() {
 }
 
 // One workgroup (index wg) of the partition launch: (head group, sequence,
-// partition), head groups fastest. TAIL = true is the grouped call's tail:
-// each sequence starts after its group's shared blocks (handled by the
+// partition), head groups fastest, over blocks of BS tokens. The partition is
+// walked in 16-token tiles whatever the block size (a tile is one 16-token
+// block, half a 32-token block or two 8-token blocks): wave w reads tokens w
+// and w + 8 of every tile, each through the block table. TAIL = true is the
+// grouped call's tail:
+// each sequence starts after its group's shared-prefix tiles (handled by the
 // shared-prefix units), its partitions go to partial slots slot_base + p, and
 // every partition writes a partial (the merge always runs).
-template <typename T, int D, int PT, bool TAIL>
+template <typename T, int D, int PT, int BS, bool TAIL>
 __device__ __forceinline__ void partition_body(
     int wg, uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
@@ -33,7 +36,10 @@ __device__ __forceinline__ void partition_body(
   using E = Elem<T>;
   constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
   constexpr int HG = 64 / LPR;       // heads per wave-wide load
-  static_assert(PT % kBlockSize == 0, "partition is whole blocks");
+  constexpr int RPW = kTileTokens / kWaves;  // rows of a tile each wave reads
+  static_assert(PT % BS == 0 && PT % kTileTokens == 0, "partition is whole blocks and tiles");
+  static_assert(BS % 8 == 0 && RPW == 2, "tile rows w and w + 8 are in blocks of >= 8 tokens");
+  static_assert(PT / BS <= 64, "a partition's table entries fit one per lane");
 
   const int H = num_heads;
   const int groups = (H + HG - 1) / HG;
@@ -43,12 +49,13 @@ __device__ __forceinline__ void partition_body(
   const int p = sp / num_seqs;
   const int ctx = context_lens[s];
   int tok0 = 0;   // first token this launch covers for sequence s
-  if constexpr (TAIL) tok0 = shared_blocks[group_of(s, group_start, num_groups)] * kBlockSize;
+  if constexpr (TAIL)
+    tok0 = shared_prefix_tokens(shared_blocks[group_of(s, group_start, num_groups)], BS);
   const int tok_begin = tok0 + p * PT;
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + PT);
-  const int blk_begin = tok_begin / kBlockSize;
-  const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
+  // tok0 (a multiple of 16) and PT are multiples of the tile and the block
+  const int ntiles = (tok_end - tok_begin + kTileTokens - 1) / kTileTokens;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -59,9 +66,15 @@ __device__ __forceinline__ void partition_body(
   const int hr = head_ok ? h : 0;     // lanes past the last head read head 0 and are ignored
 
   const uint4 qv = *reinterpret_cast<const uint4*>(query + ((size_t)s * H + hr) * D + c * 8);
-  const int32_t* bt = block_tables + (size_t)s * max_blocks + blk_begin;
+  // The partition's table entries, one per lane (at most 64), loaded once;
+  // the loop reads them with v_readlane (no memory latency per step).
+  const uint32_t blk0 = (uint32_t)tok_begin / BS;
+  const int nblk = (tok_end - tok_begin + BS - 1) / BS;
+  const int32_t table_lane =
+      lane < nblk ? block_tables[(size_t)s * max_blocks + blk0 + lane] : 0;
   const uint32_t kv_dim = (uint32_t)H * D;
-  const size_t blk_bytes = (size_t)kBlockSize * kv_dim * sizeof(uint16_t);
+  const size_t blk_bytes = (size_t)BS * kv_dim * sizeof(uint16_t);
+  const uint32_t row_bytes = kv_dim * (uint32_t)sizeof(uint16_t);
   const uint32_t col_bytes = ((uint32_t)hr * D + (uint32_t)c * 8) * sizeof(uint16_t);
   const char* kpool = reinterpret_cast<const char*>(key_cache);
   const char* vpool = reinterpret_cast<const char*>(value_cache);
@@ -71,35 +84,37 @@ __device__ __forceinline__ void partition_body(
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
-  for (int b = 0; b < nblk; ++b) {
-    const int phys = bt[b];
-    const int rows = min(kBlockSize, ctx - (blk_begin + b) * kBlockSize);
-    const char* kb = kpool + (size_t)phys * blk_bytes;
-    const char* vb = vpool + (size_t)phys * blk_bytes;
-    // Rows past the context re-read row 0 of the block (a valid token, a
-    // cache hit) instead of branching; their weight is exactly 0 below.
-    uint4 kr[kRowsPerWave], vr[kRowsPerWave];
+  for (int k = 0; k < ntiles; ++k) {
+    const int tb = tok_begin + k * kTileTokens;   // < ctx
+    // Token tb + wave + 8i, wave-uniform. Tokens past the context re-read the
+    // tile's first token (valid, a cache hit) instead of branching; their
+    // weight is exactly 0 below. Address: the block's base (64-bit, scalar)
+    // plus the row and the lane's column (32-bit).
+    uint4 kr[RPW], vr[RPW];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int row = wave + i * kWaves;
-      const uint32_t rr = row < rows ? (uint32_t)row : 0u;
-      const uint32_t off = rr * kv_dim * (uint32_t)sizeof(uint16_t) + col_bytes;
-      kr[i] = *reinterpret_cast<const uint4*>(kb + off);
-      vr[i] = *reinterpret_cast<const uint4*>(vb + off);
+    for (int i = 0; i < RPW; ++i) {
+      const uint32_t t = (uint32_t)(tb + wave + i * kWaves);
+      const uint32_t te = t < (uint32_t)ctx ? t : (uint32_t)tb;
+      // At block sizes >= 16 the whole tile sits in the block of tb.
+      const uint32_t bi = (BS >= kTileTokens ? (uint32_t)tb : te) / BS - blk0;
+      const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(table_lane, bi);
+      const uint32_t off = (te % BS) * row_bytes + col_bytes;
+      kr[i] = *reinterpret_cast<const uint4*>(kpool + (size_t)phys * blk_bytes + off);
+      vr[i] = *reinterpret_cast<const uint4*>(vpool + (size_t)phys * blk_bytes + off);
     }
-    float sc[kRowsPerWave];
+    float sc[RPW];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
+    for (int i = 0; i < RPW; ++i) {
       float d = E::dot2(kr[i].x, qv.x, 0.f);
       d = E::dot2(kr[i].y, qv.y, d);
       d = E::dot2(kr[i].z, qv.z, d);
       d = E::dot2(kr[i].w, qv.w, d);
       d = group_sum<LPR>(d);
-      sc[i] = (wave + i * kWaves < rows) ? d * scale_log2 : -INFINITY;
+      sc[i] = (tb + wave + i * kWaves < ctx) ? d * scale_log2 : -INFINITY;
     }
     float bm = sc[0];
 #pragma unroll
-    for (int i = 1; i < kRowsPerWave; ++i) bm = fmaxf(bm, sc[i]);
+    for (int i = 1; i < RPW; ++i) bm = fmaxf(bm, sc[i]);
     const float mn = fmaxf(m, bm);
     // While a stream has seen no valid row, m and mn are -inf; using 0 as the
     // reference then makes every weight 2^-inf = 0 without a branch (a
@@ -110,7 +125,7 @@ __device__ __forceinline__ void partition_body(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= alpha;
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
+    for (int i = 0; i < RPW; ++i) {
       const float pw = fast_exp2(sc[i] - ref);
       l += pw;
       acc[0] += pw * E::lo(vr[i].x);

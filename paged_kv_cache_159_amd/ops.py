@@ -7,12 +7,15 @@ library's kernels; nothing here computes on the tensors.
 
 Tensor layouts (see include/paged_kv.h):
   query, out         [num_seqs, num_heads, head_dim]          float16 | bfloat16
-  key/value_cache    [num_blocks, block_size, num_heads, head_dim]
+  key/value_cache    [num_blocks, block_size, num_heads, head_dim]  (block_size 8, 16 or 32)
   block_tables       int32 [num_seqs, max_blocks_per_seq]
   context_lens       int32 [num_seqs]
   key, value         [num_tokens, num_heads, head_dim]
   slot_mapping       int64 [num_tokens]
   block_mapping      int32 [num_pairs, 2]  (src, dst)
+
+Functions that take the caches read the block size from their shape; a
+``block_size`` argument, if given, must agree with it.
 """
 
 from __future__ import annotations
@@ -68,6 +71,13 @@ def alloc_workspace(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_siz
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
+def _block_size(key_cache, block_size):
+    bs = key_cache.shape[1] if key_cache.dim() == 4 else -1
+    if block_size is not None and block_size != bs:
+        raise ValueError(f"block_size {block_size} disagrees with the cache's {bs}")
+    return bs
+
+
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, block_size):
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
     dt = _dtype_code(out, query, key_cache, value_cache)
@@ -77,18 +87,20 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
         raise ValueError("query [S,H,D] and caches [NB,bs,H,D] expected")
     S, H, D = query.shape
     NB, bs, H2, D2 = key_cache.shape
-    if out.shape != query.shape or (H2, D2) != (H, D) or bs != block_size:
+    _block_size(key_cache, block_size)
+    if out.shape != query.shape or (H2, D2) != (H, D):
         raise ValueError("out/query/cache shapes disagree")
     if block_tables.shape[0] != S or context_lens.shape[0] != S:
         raise ValueError("block_tables and context_lens need one row per sequence")
-    return dt, S, H, D, NB, block_tables.shape[1]
+    return dt, S, H, D, NB, block_tables.shape[1], bs
 
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens,
-                           scale: float, block_size: int = 16, workspace=None) -> torch.Tensor:
+                           scale: float, block_size: int | None = None,
+                           workspace=None) -> torch.Tensor:
     """Decode attention into ``out`` (both launches). Returns ``out``."""
-    dt, S, H, D, NB, MB = _decode_args(out, query, key_cache, value_cache, block_tables,
-                                       context_lens, block_size)
+    dt, S, H, D, NB, MB, block_size = _decode_args(out, query, key_cache, value_cache,
+                                                   block_tables, context_lens, block_size)
     if workspace is None:
         workspace = alloc_workspace(S, H, D, MB, block_size, out.device)
     rc = lib().paged_attention_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
@@ -107,12 +119,13 @@ def grouped_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
 
 
 def paged_attention_decode_grouped(out, query, key_cache, value_cache, block_tables, context_lens,
-                                   group_start, shared_blocks, scale: float, block_size: int = 16,
+                                   group_start, shared_blocks, scale: float,
+                                   block_size: int | None = None,
                                    workspace=None) -> torch.Tensor:
     """Decode attention with shared prefix blocks read once per group (MFMA).
     group_start: int32 [G+1]; shared_blocks: int32 [G] (see include/paged_kv.h)."""
-    dt, S, H, D, NB, MB = _decode_args(out, query, key_cache, value_cache, block_tables,
-                                       context_lens, block_size)
+    dt, S, H, D, NB, MB, block_size = _decode_args(out, query, key_cache, value_cache,
+                                                   block_tables, context_lens, block_size)
     _on_gpu(out, group_start, shared_blocks)
     _expect(group_start, torch.int32, 1, "group_start")
     _expect(shared_blocks, torch.int32, 1, "shared_blocks")
@@ -133,9 +146,9 @@ def paged_attention_decode_grouped(out, query, key_cache, value_cache, block_tab
 
 def paged_attention_decode_partitions(out, query, key_cache, value_cache, block_tables,
                                       context_lens, scale: float, workspace,
-                                      block_size: int = 16) -> None:
-    dt, S, H, D, NB, MB = _decode_args(out, query, key_cache, value_cache, block_tables,
-                                       context_lens, block_size)
+                                      block_size: int | None = None) -> None:
+    dt, S, H, D, NB, MB, block_size = _decode_args(out, query, key_cache, value_cache,
+                                                   block_tables, context_lens, block_size)
     rc = lib().paged_attention_decode_partitions(
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), S, H, D, NB, block_size, MB,
@@ -155,7 +168,8 @@ def paged_attention_decode_merge(out, context_lens, max_blocks_per_seq: int, wor
     check("paged_attention_decode_merge", rc)
 
 
-def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, block_size: int = 16):
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+                      block_size: int | None = None):
     """Scatter new tokens' K/V rows into their slots (in place)."""
     _on_gpu(key, value, key_cache, value_cache, slot_mapping)
     dt = _dtype_code(key, value, key_cache, value_cache)
@@ -164,7 +178,8 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, block_si
         raise ValueError("key/value [T,H,D] and caches [NB,bs,H,D] expected")
     T, H, D = key.shape
     NB, bs, H2, D2 = key_cache.shape
-    if value_cache.shape != key_cache.shape or (H2, D2) != (H, D) or bs != block_size:
+    block_size = _block_size(key_cache, block_size)
+    if value_cache.shape != key_cache.shape or (H2, D2) != (H, D):
         raise ValueError("key/value and cache shapes disagree")
     if slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping needs one entry per token")
@@ -174,7 +189,7 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, block_si
     check("reshape_and_cache", rc)
 
 
-def copy_blocks(key_cache, value_cache, block_mapping, block_size: int = 16):
+def copy_blocks(key_cache, value_cache, block_mapping, block_size: int | None = None):
     """Copy whole blocks src -> dst in both pools (in place)."""
     _on_gpu(key_cache, value_cache, block_mapping)
     dt = _dtype_code(key_cache, value_cache)
@@ -184,8 +199,7 @@ def copy_blocks(key_cache, value_cache, block_mapping, block_size: int = 16):
     if block_mapping.shape[0] and block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [P, 2]")
     NB, bs, H, D = key_cache.shape
-    if bs != block_size:
-        raise ValueError("cache block size disagrees with block_size")
+    block_size = _block_size(key_cache, block_size)
     rc = lib().copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), block_mapping.data_ptr(),
                            block_mapping.shape[0], H, D, NB, block_size, dt, _stream(key_cache))
     check("copy_blocks", rc)

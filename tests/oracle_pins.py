@@ -149,9 +149,11 @@ def pin_bruteforce(pa):
 def pin_contiguous(pa):
     """Paged decode equals the library attention over the contiguous rows.
     The rows were placed through the allocator's slots, and every other slot
-    holds NaN, so a wrong translation or a read past the context shows."""
-    for dtype, H, D in (("f16", 3, 64), ("bf16", 2, 128)):
-        c = paged_case(21, [1, 15, 16, 17, 40, 70], H, D, dtype)
+    holds NaN, so a wrong translation or a read past the context shows. At
+    block sizes 8, 16 and 32, with contexts on both sides of block edges."""
+    for dtype, H, D, bs in (("f16", 3, 64, 16), ("bf16", 2, 128, 16), ("f16", 2, 64, 8),
+                            ("bf16", 3, 64, 32)):
+        c = paged_case(21 + bs, [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 40, 70], H, D, dtype, bs=bs)
         scale = 1.0 / math.sqrt(D)
         out = pa.paged_attention_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], scale,
                                         c["bs"], dtype)
@@ -162,7 +164,7 @@ def pin_contiguous(pa):
             q = _torch_upcast(c["q"][s], dtype)
             for h in range(H):
                 want = _sdpa(q[h], K[:, h], V[:, h], scale)
-                assert np.allclose(out[s, h], want, rtol=0, atol=1e-12), (dtype, s, h)
+                assert np.allclose(out[s, h], want, rtol=0, atol=1e-12), (dtype, bs, s, h)
 
 
 def pin_permutation(pa):
@@ -214,9 +216,15 @@ def pin_partitioned(pa):
 
 def pin_reshape_and_cache(co):
     """Round trip: a written token read back through its slot has the same
-    bits; every other slot is untouched; padding slots (-1) are skipped."""
-    rng = np.random.default_rng(31)
-    H, D, bs = 2, 64, 16
+    bits; every other slot is untouched; padding slots (-1) are skipped.
+    At block sizes 8, 16 and 32."""
+    for bs in (8, 16, 32):
+        _reshape_round_trip(co, bs)
+
+
+def _reshape_round_trip(co, bs):
+    rng = np.random.default_rng(31 + bs)
+    H, D = 2, 64
     alloc = BlockAllocator(12, bs, free_order=rng.permutation(12))
     lens = [5, 16, 31]
     for s, n in enumerate(lens):

@@ -67,7 +67,12 @@ def test_workspace_size(L):
         assert L.paged_attention_workspace_size(S, H, D, MB, 16) == _expected_workspace(S, H, D, MB)
     assert _expected_workspace(64, 32, 128, 128) == 64 * 32 * 8 * 8 + 64 * 32 * 8 * 512
     assert L.paged_attention_workspace_size(8, 32, 96, 2048, 16) == 0  # invalid -> 0
-    assert L.paged_attention_workspace_size(8, 32, 128, 2048, 8) == 0
+    for bs in (8, 32):                                                   # the other block sizes
+        for S, H, D, MB in ((4, 4, 64, 32), (4, 4, 64, 33), (64, 32, 128, 256), (8, 32, 128, 4096)):
+            assert L.paged_attention_workspace_size(S, H, D, MB, bs) == \
+                _expected_workspace(S, H, D, MB, bs), (bs, S, H, D, MB)
+    for bs in (0, 4, 12, 24, 64, -16):
+        assert L.paged_attention_workspace_size(8, 32, 128, 2048, bs) == 0, bs
 
 
 def _decode(L, fn="paged_attention_decode", **kw):
@@ -82,7 +87,8 @@ def _decode(L, fn="paged_attention_decode", **kw):
 @pytest.mark.parametrize("fn", ["paged_attention_decode", "paged_attention_decode_partitions"])
 def test_decode_validation(L, fn):
     assert _decode(L, fn, dt=2) == UNSUP
-    assert _decode(L, fn, bs=32) == UNSUP
+    for bs in (0, 4, 12, 64):                  # 8, 16 and 32 are the supported sizes
+        assert _decode(L, fn, bs=bs) == UNSUP
     assert _decode(L, fn, D=96) == UNSUP
     assert _decode(L, fn, H=0) == SHAPE
     assert _decode(L, fn, NB=0) == SHAPE
@@ -119,6 +125,64 @@ def test_merge_validation(L):
     assert m(P, P, 0, 4, 64, 16, 64, 0, P, need, 0) == OK
 
 
+def _expected_grouped_workspace(S, H, D, MB, bs=16):
+    """Chunk slots of 8 tiles of 16 shared tokens, then the tail partitions
+    (same partition rule as the plain call); one workspace layout."""
+    tokens = MB * bs
+    pt = 256 if tokens <= 4096 else 512
+    n = S * H * (-(-tokens // 128) + -(-tokens // pt))
+    return ((n * 8 + 255) // 256) * 256 + n * D * 4
+
+
+def test_grouped_workspace_size(L):
+    f = L.paged_attention_grouped_workspace_size
+    for bs in (8, 16, 32):
+        for S, H, D, MB in ((4, 4, 64, 1), (128, 32, 128, 37), (16, 32, 128, 256), (3, 5, 64, 1000)):
+            assert f(S, H, D, MB, bs) == _expected_grouped_workspace(S, H, D, MB, bs), (bs, S, MB)
+    assert f(4, 4, 96, 8, 16) == 0
+    assert f(4, 4, 64, 8, 12) == 0
+    assert f(4, 4, 64, 0, 16) == 0
+
+
+def _grouped(L, **kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, cl=P, gs=P, sb=P, G=1, S=4, H=4, D=64, NB=32, bs=16, MB=4,
+             scale=0.125, dt=0, ws=0, wsb=0, stream=0)
+    a.update(kw)
+    return L.paged_attention_decode_grouped(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["gs"], a["sb"], a["G"], a["S"],
+        a["H"], a["D"], a["NB"], a["bs"], a["MB"], a["scale"], a["dt"], a["ws"], a["wsb"],
+        a["stream"])
+
+
+def test_grouped_validation(L):
+    # The grouped call always needs a workspace, so every call below that gets
+    # past the argument checks stops at the workspace check, before any launch.
+    need = L.paged_attention_grouped_workspace_size(4, 4, 64, 4, 16)
+    assert need > 0
+    assert _grouped(L, dt=2) == UNSUP
+    for bs in (0, 4, 12, 64):
+        assert _grouped(L, bs=bs) == UNSUP
+    assert _grouped(L, D=96) == UNSUP
+    assert _grouped(L, H=0) == SHAPE
+    assert _grouped(L, NB=0) == SHAPE
+    assert _grouped(L, S=-1) == SHAPE
+    assert _grouped(L, MB=0) == SHAPE
+    assert _grouped(L, G=0) == SHAPE                       # sequences but no group
+    assert _grouped(L, G=-1) == SHAPE
+    assert _grouped(L, MB=2 ** 28) == SHAPE
+    assert _grouped(L, scale=float("nan")) == SHAPE
+    for name in ("out", "q", "k", "v", "bt", "cl", "gs", "sb"):
+        assert _grouped(L, **{name: 0}) == NULL, name
+    for name in ("out", "q", "k", "v"):
+        assert _grouped(L, **{name: MIS}) == ALIGN, name
+    for name in ("bt", "cl", "gs", "sb"):
+        assert _grouped(L, **{name: P + 2}) == ALIGN, name
+    assert _grouped(L) == WS
+    assert _grouped(L, ws=P, wsb=need - 1) == WS
+    assert _grouped(L, ws=MIS, wsb=need) == ALIGN
+    assert _grouped(L, S=0, G=0) == OK                     # nothing to do, nothing launched
+
+
 def test_reshape_and_cache_validation(L):
     f = L.reshape_and_cache
     base = [P, P, P, P, P, 3, 4, 64, 32, 16, 0, 0]
@@ -129,7 +193,8 @@ def test_reshape_and_cache_validation(L):
         return f(*a)
 
     assert call(10, 5) == UNSUP
-    assert call(9, 8) == UNSUP
+    assert call(9, 4) == UNSUP
+    assert call(9, 64) == UNSUP
     assert call(7, 80) == UNSUP
     assert call(6, 0) == SHAPE
     assert call(8, 0) == SHAPE

@@ -35,11 +35,13 @@ def gpu_step(w, dw, two_stage=False):
     if len(w.copy_pairs):
         pkv.copy_blocks(dw.key_cache, dw.value_cache, dw.copy_pairs)
     pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
-    ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                             w.block_size)
     if two_stage:
         pkv.paged_attention_decode_partitions(dw.out, dw.query, dw.key_cache, dw.value_cache,
                                               dw.block_tables, dw.context_lens, w.scale, ws)
-        pkv.paged_attention_decode_merge(dw.out, dw.context_lens, w.max_blocks_per_seq, ws)
+        pkv.paged_attention_decode_merge(dw.out, dw.context_lens, w.max_blocks_per_seq, ws,
+                                         block_size=w.block_size)
     else:
         pkv.paged_attention_decode(dw.out, dw.query, dw.key_cache, dw.value_cache,
                                    dw.block_tables, dw.context_lens, w.scale, workspace=ws)
@@ -88,7 +90,7 @@ def assert_attention_close(got, want, pairs=None, what="", format_bound=None):
 
 
 def check_full_step(w, pairs=None, check_caches=True, two_stage=False, format_bound=None):
-    say(f"config {w.index} {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} {w.dtype} "
+    say(f"config {w.index} {w.name}: bs={w.block_size} S={w.num_seqs} H={w.num_heads} D={w.head_dim} {w.dtype} "
         f"NB={w.num_blocks} MB={w.max_blocks_per_seq} T={len(w.slot_mapping)} "
         f"pairs={len(w.copy_pairs)} two_stage={two_stage}")
     dw = upload(w)
@@ -277,7 +279,7 @@ def grouped_step(w, dw, shared_blocks=None, group_start=None):
 
 
 def check_grouped(w, shared_blocks=None, group_start=None, format_bound=None, check_caches=True):
-    say(f"grouped {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} {w.dtype} "
+    say(f"grouped {w.name}: bs={w.block_size} S={w.num_seqs} H={w.num_heads} D={w.head_dim} {w.dtype} "
         f"groups={len(w.group_start if group_start is None else group_start) - 1} "
         f"shared={(w.shared_blocks if shared_blocks is None else shared_blocks)[:4]}")
     dw = upload(w)
@@ -348,3 +350,61 @@ def test_grouped_deterministic():
     dw2 = upload(w)
     grouped_step(w, dw2)
     assert np.array_equal(device_to_bits(dw2.out), a)
+
+
+# ------------------------------------------------------------ block sizes 8 and 32
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_block_size_step(bs, index):
+    """The workloads' context lengths over 8- or 32-token blocks (pools and
+    tables rebuilt by the allocator at that size), plain decode path."""
+    check_full_step(make_config(index, bs))
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_long_context_sampled(bs):
+    w = make_config(5, bs)
+    rng = np.random.default_rng(bs)
+    pairs = [(s, int(h)) for s in range(w.num_seqs) for h in rng.choice(w.num_heads, 2, replace=False)]
+    check_full_step(w, pairs=pairs)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dtype,head_dim", [("f16", 128), ("bf16", 64)])
+def test_block_size_edge_contexts(bs, dtype, head_dim):
+    """Block and partition boundaries at the other block sizes, with NaN
+    canaries in every unused slot (output bit-identical to the clean run)."""
+    w = make_decode_case(EDGE_CTX, 3, head_dim, dtype, seed=bs + head_dim, max_blocks=2048 // bs,
+                         block_size=bs)
+    bound = "bf16" if dtype == "bf16" else None
+    _, clean = check_full_step(w, format_bound=bound)
+    _, poisoned = check_full_step(poison_unused(w), check_caches=False, format_bound=bound)
+    assert np.array_equal(clean, poisoned)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_grouped_shared_prefix(bs):
+    """Shared-prefix workload over 8-token blocks (41 shared blocks: an odd
+    last block goes with the tails, no CoW) and 32-token blocks (10 shared
+    blocks, each two MFMA tiles; CoW of the partial 11th block)."""
+    check_grouped(make_config(4, bs))
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_grouped_singleton_groups(bs):
+    """One sequence per group sharing all its full blocks but the last: odd
+    shared-block counts at block size 8 leave half a tile to the tail."""
+    w = make_decode_case([17, 64, 300, 1000, 2048, 33, 9], 4, 128, "f16", seed=22 + bs,
+                         max_blocks=2048 // bs, block_size=bs)
+    gs = np.arange(w.num_seqs + 1, dtype=np.int32)
+    sb = ((w.context_lens - 1) // bs).astype(np.int32)
+    check_grouped(w, shared_blocks=sb, group_start=gs)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_two_stage_equals_single_call(bs):
+    w = make_config(2, bs)
+    dw1, a = check_full_step(w)
+    dw2, b = check_full_step(w, two_stage=True)
+    assert np.array_equal(device_to_bits(dw1.out), device_to_bits(dw2.out))

@@ -108,3 +108,35 @@ def test_poison_keeps_valid_tokens(small):
     assert np.isfinite(outs[1]).all()
     assert np.array_equal(outs[0], outs[1])
     assert np.isnan(oracle.upcast(p.key_cache, "f16")).sum() > 0
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_variants(bs):
+    """The same workloads over 8- and 32-token blocks: same context lengths,
+    tables of ceil(ctx / bs) valid entries, slots that match the oracle's
+    translation at that block size, prefix blocks shared within each group."""
+    for i in (1, 4):
+        w, w16 = make_config(i, bs), make_config(i)
+        assert w.block_size == bs and w.key_cache.shape[1] == bs
+        assert np.array_equal(w.context_lens, w16.context_lens)
+        kv_dim = w.num_heads * w.head_dim
+        for s in range(w.num_seqs):
+            n = oracle.num_logical_blocks(int(w.context_lens[s]), bs)
+            row = w.block_tables[s]
+            assert (row[:n] >= 0).all() and (row[:n] < w.num_blocks).all() and (row[n:] == -1).all()
+        first = 328 if i == 4 else None
+        k = 0
+        for s in range(w.num_seqs):
+            lo = first if first is not None else int(w.context_lens[s]) - 1
+            for pos in range(lo, int(w.context_lens[s])):
+                off = oracle.element_offset(w.block_tables[s], pos, bs, kv_dim)
+                assert off // kv_dim == w.slot_mapping[k]
+                k += 1
+        assert k == len(w.slot_mapping)
+        w.allocator.check_invariants()
+    w = make_config(4, bs)
+    assert (w.shared_blocks == 328 // bs).all()
+    assert len(w.copy_pairs) == (0 if 328 % bs == 0 else 112)
+    for g in range(16):
+        t = w.block_tables[g * 8:(g + 1) * 8, :328 // bs]
+        assert (t == t[0]).all()

@@ -122,15 +122,16 @@ def _finish(index, name, dtype, H, D, alloc, seqs, ctx, MB, streams, new_tokens,
             slots, pairs, group_start=None, shared_blocks=None):
     S = len(seqs)
     NB = alloc.num_blocks
+    bs = alloc.block_size
     T = len(slots)
     q = _normal_bits(streams[2], S * H * D, dtype).reshape(S, H, D)
-    kc = _normal_bits(streams[3], NB * BLOCK_SIZE * H * D, dtype).reshape(NB, BLOCK_SIZE, H, D)
-    vc = _normal_bits(streams[4], NB * BLOCK_SIZE * H * D, dtype).reshape(NB, BLOCK_SIZE, H, D)
+    kc = _normal_bits(streams[3], NB * bs * H * D, dtype).reshape(NB, bs, H, D)
+    vc = _normal_bits(streams[4], NB * bs * H * D, dtype).reshape(NB, bs, H, D)
     nk = _normal_bits(streams[5], T * H * D, dtype).reshape(T, H, D)
     nv = _normal_bits(streams[6], T * H * D, dtype).reshape(T, H, D)
     return Workload(
         index=index, name=name, dtype=dtype, num_seqs=S, num_heads=H, head_dim=D,
-        block_size=BLOCK_SIZE, num_blocks=NB, max_blocks_per_seq=MB,
+        block_size=bs, num_blocks=NB, max_blocks_per_seq=MB,
         scale=float(np.float32(1.0 / math.sqrt(D))),
         query=q, key_cache=kc, value_cache=vc,
         block_tables=alloc.tables_array(seqs, MB),
@@ -142,18 +143,18 @@ def _finish(index, name, dtype, H, D, alloc, seqs, ctx, MB, streams, new_tokens,
     )
 
 
-def _blocks(tokens: int) -> int:
-    return (tokens + BLOCK_SIZE - 1) // BLOCK_SIZE
+def _blocks(tokens: int, bs: int = BLOCK_SIZE) -> int:
+    return (tokens + bs - 1) // bs
 
 
-def _decode_batch(index, name, dtype, H, D, ctx, MB, streams, pool=None):
+def _decode_batch(index, name, dtype, H, D, ctx, MB, streams, pool=None, bs=BLOCK_SIZE):
     """Sequences hold ctx-1 tokens; the step writes token ctx-1 of each."""
     S = len(ctx)
-    needed = sum(_blocks(int(c)) for c in ctx)
+    needed = sum(_blocks(int(c), bs) for c in ctx)
     if pool is None:
         pool = math.ceil(1.1 * needed)
     order = np.random.Generator(np.random.PCG64(streams[1])).permutation(pool)
-    alloc = BlockAllocator(pool, BLOCK_SIZE, free_order=order)
+    alloc = BlockAllocator(pool, bs, free_order=order)
     seqs = list(range(S))
     for s in seqs:
         alloc.allocate(s, int(ctx[s]) - 1)
@@ -166,7 +167,8 @@ def _decode_batch(index, name, dtype, H, D, ctx, MB, streams, pool=None):
 
 
 def make_decode_case(ctx, num_heads: int, head_dim: int, dtype: str = "f16", seed: int = 0,
-                     max_blocks: int | None = None, pool: int | None = None) -> Workload:
+                     max_blocks: int | None = None, pool: int | None = None,
+                     block_size: int = BLOCK_SIZE) -> Workload:
     """A decode step over the given context lengths (each sequence's last token
     is written by the step), for edge-case tests. Same recipe as the numbered
     workloads, seeded by ``seed``."""
@@ -174,33 +176,39 @@ def make_decode_case(ctx, num_heads: int, head_dim: int, dtype: str = "f16", see
     ctx = [int(c) for c in ctx]
     if min(ctx) < 1:
         raise ValueError("context lengths must be >= 1")
-    mb = max_blocks if max_blocks is not None else max(_blocks(c) for c in ctx)
-    return _decode_batch(0, "custom", dtype, num_heads, head_dim, ctx, mb, st, pool)
+    mb = max_blocks if max_blocks is not None else max(_blocks(c, block_size) for c in ctx)
+    return _decode_batch(0, "custom", dtype, num_heads, head_dim, ctx, mb, st, pool, block_size)
 
 
-def make_config(index: int) -> Workload:
-    """Build workload ``index`` (1..5). Deterministic for a given index."""
+def make_config(index: int, block_size: int = BLOCK_SIZE) -> Workload:
+    """Build workload ``index`` (1..5) over blocks of ``block_size`` tokens.
+    Deterministic for a given (index, block_size); the context lengths do not
+    depend on the block size, the pools (sized in blocks) do."""
     st = _seed_streams(index)
+    bs = block_size
     if index == 1:
         ctx = [35, 16, 1, 50]
-        return _decode_batch(1, CONFIG_NAMES[1], "f16", 4, 64, ctx, _blocks(max(ctx)), st, pool=32)
+        pool = 32 * BLOCK_SIZE // bs
+        return _decode_batch(1, CONFIG_NAMES[1], "f16", 4, 64, ctx, _blocks(max(ctx), bs), st,
+                             pool=pool, bs=bs)
     if index == 2:
         ctx = np.random.Generator(np.random.PCG64(st[0])).integers(128, 2048, size=64, endpoint=True)
-        return _decode_batch(2, CONFIG_NAMES[2], "f16", 32, 128, ctx, 2048 // BLOCK_SIZE, st)
+        return _decode_batch(2, CONFIG_NAMES[2], "f16", 32, 128, ctx, 2048 // bs, st, bs=bs)
     if index == 3:
         x = np.random.Generator(np.random.PCG64(st[0])).exponential(512.0, size=256)
         ctx = np.clip(np.rint(x), 1, 2048).astype(np.int64)
-        return _decode_batch(3, CONFIG_NAMES[3], "f16", 32, 128, ctx, 2048 // BLOCK_SIZE, st)
+        return _decode_batch(3, CONFIG_NAMES[3], "f16", 32, 128, ctx, 2048 // bs, st, bs=bs)
     if index == 4:
-        return _shared_prefix(st)
+        return _shared_prefix(st, bs=bs)
     if index == 5:
         ctx = [32768] * 8
-        return _decode_batch(5, CONFIG_NAMES[5], "f16", 32, 128, ctx, 32768 // BLOCK_SIZE, st)
+        return _decode_batch(5, CONFIG_NAMES[5], "f16", 32, 128, ctx, 32768 // bs, st, bs=bs)
     raise ValueError(f"no workload {index}")
 
 
 def _shared_prefix(st, index=4, name=CONFIG_NAMES[4], prompts=16, samples=8, prefix=328,
-                   suffix_lo=1, suffix_hi=256, H=32, D=128, dtype="bf16") -> Workload:
+                   suffix_lo=1, suffix_hi=256, H=32, D=128, dtype="bf16",
+                   bs=BLOCK_SIZE) -> Workload:
     """Each prompt's prefix is allocated once and forked to its samples
     (refcount = samples); then every sample appends its own suffix in index
     order, copying the shared, partly filled last prefix block on its first
@@ -209,9 +217,9 @@ def _shared_prefix(st, index=4, name=CONFIG_NAMES[4], prompts=16, samples=8, pre
                                                                  size=prompts * samples,
                                                                  endpoint=True)
     ctx = prefix + suffix
-    prefix_blocks = _blocks(prefix)
-    full_prefix_blocks = prefix // BLOCK_SIZE
-    partial = prefix % BLOCK_SIZE != 0
+    prefix_blocks = _blocks(prefix, bs)
+    full_prefix_blocks = prefix // bs
+    partial = prefix % bs != 0
     # blocks in use at the end: one prefix per prompt, a CoW copy of a partly
     # filled last prefix block for every writing sample but the last of each
     # prompt, and each sample's own further blocks
@@ -221,10 +229,10 @@ def _shared_prefix(st, index=4, name=CONFIG_NAMES[4], prompts=16, samples=8, pre
             writers = int((suffix[g * samples:(g + 1) * samples] > 0).sum())
             copies += max(writers - 1, 0)
     needed = prompts * prefix_blocks + copies + sum(
-        max(_blocks(int(c)) - prefix_blocks, 0) for c in ctx)
+        max(_blocks(int(c), bs) - prefix_blocks, 0) for c in ctx)
     pool = math.ceil(1.1 * needed)
     order = np.random.Generator(np.random.PCG64(st[1])).permutation(pool)
-    alloc = BlockAllocator(pool, BLOCK_SIZE, free_order=order)
+    alloc = BlockAllocator(pool, bs, free_order=order)
     seqs = list(range(prompts * samples))
     for g in range(prompts):
         alloc.allocate(g * samples, prefix)
@@ -237,7 +245,7 @@ def _shared_prefix(st, index=4, name=CONFIG_NAMES[4], prompts=16, samples=8, pre
             slots.append(slot)
             if pair is not None:
                 pairs.append(pair)
-    MB = _blocks(prefix + suffix_hi)
+    MB = _blocks(prefix + suffix_hi, bs)
     group_start = np.arange(0, prompts * samples + 1, samples, dtype=np.int32)
     shared = np.full(prompts, full_prefix_blocks, dtype=np.int32)
     return _finish(index, name, dtype, H, D, alloc, seqs, ctx, MB, st, len(slots),
@@ -245,12 +253,12 @@ def _shared_prefix(st, index=4, name=CONFIG_NAMES[4], prompts=16, samples=8, pre
 
 
 def make_shared_case(prompts, samples, prefix, suffix_lo, suffix_hi, num_heads, head_dim,
-                     dtype="f16", seed=0) -> Workload:
+                     dtype="f16", seed=0, block_size=BLOCK_SIZE) -> Workload:
     """A shared-prefix decode step (the recipe of the parallel-sampling
     workload) with free sizes, for edge-case tests."""
     st = np.random.SeedSequence(seed).spawn(8)
     return _shared_prefix(st, 0, "custom_shared", prompts, samples, prefix, suffix_lo, suffix_hi,
-                          num_heads, head_dim, dtype)
+                          num_heads, head_dim, dtype, block_size)
 
 
 def poison_unused(w: Workload) -> Workload:
