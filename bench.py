@@ -62,6 +62,11 @@ def parse():
                     help="turn rocprofv3 counter_collection.csv files (FETCH_SIZE and WRITE_SIZE "
                          "runs of this bench, then of --calibrate-copy) into "
                          "profiles/traffic_<workload>.json and .md, and exit (no GPU needed)")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swap_blocks instead: half of the workload's sequences "
+                         "swapped out to pinned host pools and back (one launch each way), "
+                         "next to a contiguous pinned copy of the same bytes; prints its own "
+                         "JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -233,6 +238,82 @@ def traffic_summary(paths, w, grouped):
     print(json.dumps(res, indent=1))
 
 
+PCIE5_X16_GBS = 64.0   # host link of the MI355X platform: PCIe 5.0 x16, per direction
+
+
+def swap_bench(args, w, dw, dev):
+    """swap_blocks bandwidth: device -> pinned host and back, for every other
+    sequence's blocks, timed with HIP events on the launch stream."""
+    import torch
+
+    import paged_kv_cache_159_amd as pkv
+    from workloads import SwapSpace
+
+    alloc = w.allocator
+    seqs = list(range(0, w.num_seqs, 2))
+    nhost = sum(len(alloc.block_table(s)) for s in seqs)
+    sw = SwapSpace(alloc, nhost)
+    out_pairs = np.concatenate([sw.swap_out(s) for s in seqs]).astype(np.int32)
+    in_pairs = np.concatenate([sw.swap_in(s) for s in seqs]).astype(np.int32)
+    shape = (nhost,) + tuple(dw.key_cache.shape[1:])
+    hk = torch.empty(shape, dtype=dw.key_cache.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=dw.key_cache.dtype, pin_memory=True)
+    mo = torch.from_numpy(out_pairs).to(dev)
+    mi = torch.from_numpy(in_pairs).to(dev)
+    nbytes = 2 * len(out_pairs) * w.block_size * w.num_heads * w.head_dim * 2
+    flat_dev = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    flat_host = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+    n = max(5, min(args.steps, 50))
+    t_out = timed(lambda: pkv.swap_blocks(dw.key_cache, dw.value_cache, hk, hv, mo), n)
+    t_in = timed(lambda: pkv.swap_blocks(hk, hv, dw.key_cache, dw.value_cache, mi), n)
+    mo_h, mi_h = torch.from_numpy(out_pairs), torch.from_numpy(in_pairs)
+    t_out_dma = timed(lambda: pkv.swap_blocks(dw.key_cache, dw.value_cache, hk, hv, mo_h,
+                                              method="dma"), n)
+    t_in_dma = timed(lambda: pkv.swap_blocks(hk, hv, dw.key_cache, dw.value_cache, mi_h,
+                                             method="dma"), n)
+    runs_out = 1 + int(np.count_nonzero(np.any(np.diff(out_pairs, axis=0) != 1, axis=1)))
+    runs_in = 1 + int(np.count_nonzero(np.any(np.diff(in_pairs, axis=0) != 1, axis=1)))
+    t_d2h = timed(lambda: flat_host.copy_(flat_dev, non_blocking=True), n)
+    t_h2d = timed(lambda: flat_dev.copy_(flat_host, non_blocking=True), n)
+    gbs = lambda t: nbytes / t / 1e9
+    res = {
+        "metric": "swap_blocks host-link GB/s (swap-out, swap-in)",
+        "value": round(gbs(t_out), 2),
+        "unit": "GB/s",
+        "swap_in_gbs": round(gbs(t_in), 2),
+        "blocks_per_direction": int(len(out_pairs)),
+        "bytes_per_direction": int(nbytes),
+        "swap_out_ms": round(t_out * 1e3, 3),
+        "swap_in_ms": round(t_in * 1e3, 3),
+        "dma": {"swap_out_gbs": round(gbs(t_out_dma), 2), "swap_in_gbs": round(gbs(t_in_dma), 2),
+                "copies_per_pool": {"out": runs_out, "in": runs_in}},
+        "contiguous_pinned_copy_gbs": {"d2h": round(gbs(t_d2h), 2), "h2d": round(gbs(t_h2d), 2)},
+        "roofline": {"bound": "host link", "peak": PCIE5_X16_GBS, "unit": "GB/s",
+                     "frac_out": round(gbs(t_out) / PCIE5_X16_GBS, 4),
+                     "frac_in": round(gbs(t_in) / PCIE5_X16_GBS, 4)},
+        "config": {"workload": f"{w.name}: every other sequence ({len(seqs)} of {w.num_seqs}), "
+                               f"block_size {w.block_size}, {w.dtype}"},
+        "data": "synthetic",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def load_traffic(key):
     """HBM traffic per decode launch from committed rocprofv3 counter runs,
     only if they were taken on the current decode kernel source."""
@@ -318,6 +399,9 @@ def main():
           f"{w.dtype} NB={w.num_blocks} sum(ctx)={w.total_context} generated in {time.time() - t0:.1f} s",
           file=sys.stderr, flush=True)
     dw = upload(w, dev)
+    if args.swap:
+        swap_bench(args, w, dw, dev)
+        return
     pool_bytes = 2 * dw.key_cache.numel() * 2
     R = args.replicas or max(2, int(np.ceil(4.0e9 / pool_bytes)))
     R = min(R, 16)

@@ -72,7 +72,9 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = -3, /* dtype, block_size or head_dim not supported */
   PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
   PKV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
-  PKV_ERR_ALIGN = -6        /* a pointer is not 16-byte aligned */
+  PKV_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
+  PKV_ERR_MEMORY = -7       /* swap_blocks: a buffer is not device memory of the current
+                               device or pinned host memory, or is smaller than its sizes */
 } pkv_status;
 
 /* Library version, major*10000 + minor*100 + patch. */
@@ -209,6 +211,49 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
 int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping, int num_pairs,
                 int num_heads, int head_dim, int num_blocks, int block_size, int dtype,
                 void* stream);
+
+/*
+ * Swap-out / swap-in of whole blocks between a device pool and a pool in
+ * pinned host memory [P1 §3.3.3 "显存不足时的处理策略", CPU Swap: the blocks of
+ * a sequence being swapped out are copied block by block into pre-allocated
+ * host buffers and its device blocks are freed; swapping in copies them back
+ * into newly allocated device blocks; P2 "vLLM高性能推理架构的工程落地考量":
+ * the cost is bound by the host link]. For each pair (src, dst) in
+ * block_mapping, block dst of (dst_key, dst_value) becomes a bit-exact copy
+ * of block src of (src_key, src_value); both pools are laid out
+ * [num_blocks][block_size][num_heads][head_dim].
+ *   Swap-out: src = the device pools, dst = the host pools.
+ *   Swap-in:  src = the host pools,   dst = the device pools.
+ * Each pool, and block_mapping (int32 [num_pairs][2]), must be device memory
+ * of the current device or pinned host memory (hipHostMalloc, e.g. a torch
+ * tensor made with pin_memory=True); anything else, or a pool smaller than
+ * its num_blocks, returns PKV_ERR_MEMORY before any launch (checked with
+ * hipPointerGetAttributes and hipMemGetAddressRange). One launch on `stream`
+ * moves every pair; host memory is read and written by the kernel over the
+ * host link, and the kernel's writes are visible to the host once `stream`
+ * has been synchronised. Preconditions: src ids < src_num_blocks, dst ids <
+ * dst_num_blocks and unique. num_pairs == 0 is a no-op (pointers may then
+ * be NULL).
+ */
+int swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                const int32_t* block_mapping, int num_pairs, int num_heads, int head_dim,
+                int src_num_blocks, int dst_num_blocks, int block_size, int dtype, void* stream);
+
+/*
+ * The same block moves as swap_blocks, done by the DMA engines instead of a
+ * kernel [P1 §3.3.3 "CPU Swap策略": swap is page-granular and runs as DMA
+ * transfers between device and host]: one hipMemcpyAsync per pool for each
+ * run of pairs whose source and destination ids both step by one, in
+ * mapping order, on `stream`. block_mapping (int32 [num_pairs][2]) is HOST
+ * memory here (any host memory), read during the call; every id is checked
+ * against its pool (PKV_ERR_SHAPE) before the first copy. Pools as for
+ * swap_blocks (PKV_ERR_MEMORY otherwise). A failed enqueue returns
+ * PKV_ERR_LAUNCH; copies enqueued before it still run.
+ */
+int swap_blocks_dma(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                    const int32_t* block_mapping, int num_pairs, int num_heads, int head_dim,
+                    int src_num_blocks, int dst_num_blocks, int block_size, int dtype,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,4 +38,4 @@ from .paged_attention import (  # noqa: F401
     partitioned_decode_head,
     merge_partitions,
 )
-from .cache_ops import reshape_and_cache, copy_blocks  # noqa: F401
+from .cache_ops import reshape_and_cache, copy_blocks, swap_blocks  # noqa: F401

@@ -85,3 +85,36 @@ def copy_blocks(key_cache_bits, value_cache_bits, block_mapping):
         K[d] = key_cache_bits[s]
         V[d] = value_cache_bits[s]
     return K, V
+
+
+def swap_blocks(src_key_bits, src_value_bits, dst_key_bits, dst_value_bits, block_mapping):
+    """Copy whole blocks from one pool pair into another: swap-out (device pool
+    -> host pool) and swap-in (host pool -> device pool).
+
+    block_mapping  int [P, 2] rows (src block in the source pools, dst block in
+    the destination pools)
+
+    [P1 §3.3.3 "显存不足时的处理策略", CPU Swap: the blocks of a sequence being
+    swapped out are copied block by block into pre-allocated host buffers and
+    its device blocks freed; swapping in copies them back into newly
+    allocated device blocks.] Reading where the pages are silent: destination
+    blocks are unique in one call (otherwise the result would depend on copy
+    order); the function refuses duplicates. The source pools are not changed.
+    Pinned: a swap-out followed by a swap-in into other device blocks gives
+    the sequence the same attention output through its new block table, bit
+    for bit, and every block not named as a destination is unchanged.
+    """
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    if src_key_bits.shape[1:] != dst_key_bits.shape[1:]:
+        raise ValueError("source and destination blocks differ in shape")
+    if pairs.size and (pairs.min() < 0 or pairs[:, 0].max() >= src_key_bits.shape[0]
+                       or pairs[:, 1].max() >= dst_key_bits.shape[0]):
+        raise IndexError("block id outside its pool")
+    if np.unique(pairs[:, 1]).size != pairs.shape[0]:
+        raise ValueError("duplicate destination blocks")
+    K = dst_key_bits.copy()
+    V = dst_value_bits.copy()
+    for s, d in pairs.tolist():
+        K[d] = src_key_bits[s]
+        V[d] = src_value_bits[s]
+    return K, V

@@ -16,5 +16,6 @@ from .ops import (  # noqa: F401
     paged_attention_decode_merge,
     paged_attention_decode_partitions,
     reshape_and_cache,
+    swap_blocks,
     workspace_size,
 )

@@ -25,11 +25,13 @@ EXPORTS = (
     "paged_attention_decode_grouped",
     "reshape_and_cache",
     "copy_blocks",
+    "swap_blocks",
+    "swap_blocks_dma",
 )
 
 PKV_F16, PKV_BF16 = 0, 1
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_UNSUPPORTED",
-          -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_LAUNCH", -6: "PKV_ERR_ALIGN"}
+          -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_LAUNCH", -6: "PKV_ERR_ALIGN", -7: "PKV_ERR_MEMORY"}
 
 _lib = None
 
@@ -51,6 +53,8 @@ _SIGNATURES = {
                                             _f, _i, _p, _z, _p]),
     "reshape_and_cache": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "copy_blocks": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
+    "swap_blocks": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
+    "swap_blocks_dma": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
 }
 
 

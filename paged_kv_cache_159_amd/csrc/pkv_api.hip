@@ -125,6 +125,39 @@ int check_grouped(int num_seqs, int num_heads, int head_dim, int block_size,
   return PKV_OK;
 }
 
+// Device address under which the current device reaches [ptr, ptr + bytes):
+// device memory of this device, or pinned (page-locked, mapped) host memory.
+// Anything else (pageable host memory, another device's memory, a range that
+// runs past its allocation) is refused with PKV_ERR_MEMORY before any launch.
+int device_accessible(const void* ptr, size_t bytes, const void** dev_ptr) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return PKV_ERR_MEMORY;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_MEMORY;
+  if (attr.type == hipMemoryTypeDevice) {
+    if (attr.device != dev) return PKV_ERR_MEMORY;
+    *dev_ptr = ptr;
+  } else if (attr.type == hipMemoryTypeHost) {
+    if (attr.devicePointer == nullptr) return PKV_ERR_MEMORY;
+    *dev_ptr = attr.devicePointer;
+  } else {
+    return PKV_ERR_MEMORY;
+  }
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(*dev_ptr)) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKV_ERR_MEMORY;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+  const uintptr_t p = reinterpret_cast<uintptr_t>(*dev_ptr);
+  if (p < b || bytes > size || p - b > size - bytes) return PKV_ERR_MEMORY;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,6 +170,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_NULL: return "a required pointer is NULL";
     case PKV_ERR_SHAPE: return "argument out of range (count, size overflow or non-finite scale)";
     case PKV_ERR_UNSUPPORTED: return "unsupported dtype, block_size or head_dim";
+    case PKV_ERR_MEMORY:
+      return "a buffer is not device memory of the current device or pinned host memory, "
+             "or is smaller than its sizes say";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
@@ -309,8 +345,85 @@ int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping
   if (!key_cache || !value_cache || !block_mapping) return PKV_ERR_NULL;
   if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(block_mapping))
     return PKV_ERR_ALIGN;
-  return status_of(pkv::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
-                                           block_elems, static_cast<hipStream_t>(stream)));
+  return status_of(pkv::launch_copy_blocks(key_cache, value_cache, key_cache, value_cache,
+                                           block_mapping, num_pairs, block_elems, false,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                const int32_t* block_mapping, int num_pairs, int num_heads, int head_dim,
+                int src_num_blocks, int dst_num_blocks, int block_size, int dtype, void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, src_num_blocks);
+  if (rc) return rc;
+  if (dst_num_blocks < 1) return PKV_ERR_SHAPE;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  const int64_t block_elems = (int64_t)block_size * num_heads * head_dim;
+  const int64_t groups = (block_elems / 8 + pkv::kCopyVecsPerGroup - 1) / pkv::kCopyVecsPerGroup;
+  if ((int64_t)num_pairs * 2 * groups > kMaxGrid) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;  // empty tensors may carry NULL
+  if (!src_key || !src_value || !dst_key || !dst_value || !block_mapping) return PKV_ERR_NULL;
+  if (!aligned16(src_key) || !aligned16(src_value) || !aligned16(dst_key) ||
+      !aligned16(dst_value) || !aligned4(block_mapping))
+    return PKV_ERR_ALIGN;
+  const size_t block_bytes = (size_t)block_elems * sizeof(uint16_t);
+  const void *sk, *sv, *dk, *dv, *bm;
+  if ((rc = device_accessible(src_key, block_bytes * src_num_blocks, &sk)) ||
+      (rc = device_accessible(src_value, block_bytes * src_num_blocks, &sv)) ||
+      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk)) ||
+      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv)) ||
+      (rc = device_accessible(block_mapping, (size_t)num_pairs * 2 * sizeof(int32_t), &bm)))
+    return rc;
+  return status_of(pkv::launch_copy_blocks(sk, sv, const_cast<void*>(dk), const_cast<void*>(dv),
+                                           static_cast<const int32_t*>(bm), num_pairs,
+                                           block_elems, true, static_cast<hipStream_t>(stream)));
+}
+
+
+int swap_blocks_dma(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                    const int32_t* block_mapping, int num_pairs, int num_heads, int head_dim,
+                    int src_num_blocks, int dst_num_blocks, int block_size, int dtype,
+                    void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, src_num_blocks);
+  if (rc) return rc;
+  if (dst_num_blocks < 1 || num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_key || !src_value || !dst_key || !dst_value || !block_mapping) return PKV_ERR_NULL;
+  if (!aligned16(src_key) || !aligned16(src_value) || !aligned16(dst_key) ||
+      !aligned16(dst_value) || !aligned4(block_mapping))
+    return PKV_ERR_ALIGN;
+  // The mapping is host memory here: every id is checked before any copy.
+  for (int i = 0; i < num_pairs; ++i) {
+    const int32_t sb = block_mapping[2 * i], db = block_mapping[2 * i + 1];
+    if (sb < 0 || sb >= src_num_blocks || db < 0 || db >= dst_num_blocks) return PKV_ERR_SHAPE;
+  }
+  const size_t block_bytes = (size_t)block_size * num_heads * head_dim * sizeof(uint16_t);
+  const void *sk, *sv, *dk, *dv;
+  if ((rc = device_accessible(src_key, block_bytes * src_num_blocks, &sk)) ||
+      (rc = device_accessible(src_value, block_bytes * src_num_blocks, &sv)) ||
+      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk)) ||
+      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv)))
+    return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Runs of pairs whose source and destination ids both step by one become
+  // one copy per pool.
+  for (int i = 0; i < num_pairs;) {
+    const int32_t s0 = block_mapping[2 * i], d0 = block_mapping[2 * i + 1];
+    int n = 1;
+    while (i + n < num_pairs && block_mapping[2 * (i + n)] == s0 + n &&
+           block_mapping[2 * (i + n) + 1] == d0 + n)
+      ++n;
+    const size_t bytes = block_bytes * (size_t)n;
+    const size_t so = block_bytes * (size_t)s0, doff = block_bytes * (size_t)d0;
+    if (hipMemcpyAsync(static_cast<char*>(const_cast<void*>(dk)) + doff,
+                       static_cast<const char*>(sk) + so, bytes, hipMemcpyDefault, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(static_cast<char*>(const_cast<void*>(dv)) + doff,
+                       static_cast<const char*>(sv) + so, bytes, hipMemcpyDefault, st) !=
+            hipSuccess)
+      return PKV_ERR_LAUNCH;
+    i += n;
+  }
+  return PKV_OK;
 }
 
 }  // extern "C"

@@ -11,6 +11,16 @@
 // (src, dst) pair copies block_size*kv_dim elements of K and of V. A block of
 // the LLaMA-7B shape is 128 KiB per pool, so it is split over workgroups of
 // 16 KiB each; every thread issues its four 16-byte loads before its stores.
+//
+// swap_blocks [P1 §3.3.3 "显存不足时的处理策略", CPU Swap: a swapped-out
+// sequence's blocks are copied page by page to pre-allocated host buffers and
+// its device blocks freed; swapping in copies them back into newly allocated
+// device blocks; P2 "vLLM高性能推理架构的工程落地考量": swap is bound by the
+// host link]: the same block copy between two pools, one of which is pinned
+// host memory that the kernel reads or writes directly over the host link.
+// One launch moves every listed block (no per-block DMA command). The kernel
+// ends with a system-scope release so that its writes to host memory are
+// visible to the host once the stream has been synchronised.
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -40,8 +50,10 @@ reshape_and_cache_kernel(const uint4* __restrict__ key, const uint4* __restrict_
   }
 }
 
+template <bool SYSTEM_RELEASE>
 __global__ void __launch_bounds__(kCacheThreads)
-copy_blocks_kernel(uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+copy_blocks_kernel(const uint4* __restrict__ src_key, const uint4* __restrict__ src_value,
+                   uint4* __restrict__ dst_key, uint4* __restrict__ dst_value,
                    const int32_t* __restrict__ block_mapping, int64_t block_vecs,
                    int groups_per_block) {
   const int g = blockIdx.x % groups_per_block;
@@ -49,21 +61,25 @@ copy_blocks_kernel(uint4* __restrict__ key_cache, uint4* __restrict__ value_cach
   const int pair = blockIdx.x / (2 * groups_per_block);
   const int64_t src = block_mapping[2 * pair];
   const int64_t dst = block_mapping[2 * pair + 1];
-  uint4* base = pool ? value_cache : key_cache;
-  const uint4* sp = base + src * block_vecs;
-  uint4* dp = base + dst * block_vecs;
+  const uint4* sp = (pool ? src_value : src_key) + src * block_vecs;
+  uint4* dp = (pool ? dst_value : dst_key) + dst * block_vecs;
   const int64_t first = (int64_t)g * kCopyVecsPerGroup + threadIdx.x;
-  uint4 v[kCopyVecsPerThread];
-#pragma unroll
-  for (int i = 0; i < kCopyVecsPerThread; ++i) {
-    const int64_t e = first + (int64_t)i * kCacheThreads;
-    if (e < block_vecs) v[i] = sp[e];
-  }
-#pragma unroll
-  for (int i = 0; i < kCopyVecsPerThread; ++i) {
-    const int64_t e = first + (int64_t)i * kCacheThreads;
-    if (e < block_vecs) dp[e] = v[i];
-  }
+  // Loads are unconditional (indices past the block re-read its last vector)
+  // and all four are issued before the stores, so they are in flight at once.
+  static_assert(kCopyVecsPerThread == 4, "four named vectors below");
+  const int64_t e0 = first, e1 = first + kCacheThreads, e2 = first + 2 * kCacheThreads,
+                e3 = first + 3 * kCacheThreads;
+  const int64_t last = block_vecs - 1;
+  const uint4 v0 = sp[e0 < block_vecs ? e0 : last];
+  const uint4 v1 = sp[e1 < block_vecs ? e1 : last];
+  const uint4 v2 = sp[e2 < block_vecs ? e2 : last];
+  const uint4 v3 = sp[e3 < block_vecs ? e3 : last];
+  __builtin_amdgcn_sched_barrier(0);
+  if (e0 < block_vecs) dp[e0] = v0;
+  if (e1 < block_vecs) dp[e1] = v1;
+  if (e2 < block_vecs) dp[e2] = v2;
+  if (e3 < block_vecs) dp[e3] = v3;
+  if constexpr (SYSTEM_RELEASE) __threadfence_system();
 }
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -77,14 +93,22 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,
-                              int num_pairs, int64_t block_elems, hipStream_t stream) {
+hipError_t launch_copy_blocks(const void* src_key, const void* src_value, void* dst_key,
+                              void* dst_value, const int32_t* block_mapping, int num_pairs,
+                              int64_t block_elems, bool system_release, hipStream_t stream) {
   const int64_t block_vecs = block_elems / 8;
   const int groups = (int)((block_vecs + kCopyVecsPerGroup - 1) / kCopyVecsPerGroup);
   const unsigned grid = (unsigned)num_pairs * 2u * (unsigned)groups;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(grid), dim3(kCacheThreads), 0, stream,
-                     static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache),
-                     block_mapping, block_vecs, groups);
+  auto* sk = static_cast<const uint4*>(src_key);
+  auto* sv = static_cast<const uint4*>(src_value);
+  auto* dk = static_cast<uint4*>(dst_key);
+  auto* dv = static_cast<uint4*>(dst_value);
+  if (system_release)
+    hipLaunchKernelGGL(copy_blocks_kernel<true>, dim3(grid), dim3(kCacheThreads), 0, stream, sk,
+                       sv, dk, dv, block_mapping, block_vecs, groups);
+  else
+    hipLaunchKernelGGL(copy_blocks_kernel<false>, dim3(grid), dim3(kCacheThreads), 0, stream, sk,
+                       sv, dk, dv, block_mapping, block_vecs, groups);
   return hipGetLastError();
 }
 

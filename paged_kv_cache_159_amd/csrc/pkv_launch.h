@@ -58,7 +58,11 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
                                     void* value_cache, const int64_t* slot_mapping, int num_tokens,
                                     int row_elems, hipStream_t stream);
 
-hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,
-                              int num_pairs, int64_t block_elems, hipStream_t stream);
+// Block copy from (src_key, src_value) to (dst_key, dst_value): the same pools
+// for copy_blocks, a device pool and a pinned host pool for swap_blocks
+// (system_release: end with a system-scope release for the host side).
+hipError_t launch_copy_blocks(const void* src_key, const void* src_value, void* dst_key,
+                              void* dst_value, const int32_t* block_mapping, int num_pairs,
+                              int64_t block_elems, bool system_release, hipStream_t stream);
 
 }  // namespace pkv

@@ -13,6 +13,8 @@ Tensor layouts (see include/paged_kv.h):
   key, value         [num_tokens, num_heads, head_dim]
   slot_mapping       int64 [num_tokens]
   block_mapping      int32 [num_pairs, 2]  (src, dst)
+  host pools         swap_blocks only: [num_cpu_blocks, block_size, num_heads, head_dim]
+                     in pinned CPU memory (torch pin_memory=True)
 
 Functions that take the caches read the block size from their shape; a
 ``block_size`` argument, if given, must agree with it.
@@ -203,3 +205,55 @@ def copy_blocks(key_cache, value_cache, block_mapping, block_size: int | None = 
     rc = lib().copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), block_mapping.data_ptr(),
                            block_mapping.shape[0], H, D, NB, block_size, dt, _stream(key_cache))
     check("copy_blocks", rc)
+
+
+def _pool_tensor(t, name):
+    if t.device.type == "cpu" and not t.is_pinned():
+        raise ValueError(f"{name} is in pageable host memory; swap pools on the host must be "
+                         "pinned (pin_memory=True)")
+    if t.device.type not in ("cpu", "cuda"):
+        raise ValueError(f"{name} must be a GPU tensor or a pinned CPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, method: str = "kernel"):
+    """Copy whole blocks src -> dst from the (src_key, src_value) pools into the
+    (dst_key, dst_value) pools, one of which lives in pinned host memory:
+    swap-out (device -> host) or swap-in (host -> device), on the current
+    stream of the GPU involved.
+    method "kernel": one launch; ``block_mapping`` int32 [P, 2] on that GPU or
+    pinned. method "dma": DMA copies per run of consecutive blocks;
+    ``block_mapping`` int32 [P, 2] on the CPU (read during the call)."""
+    if method not in ("kernel", "dma"):
+        raise ValueError("method must be 'kernel' or 'dma'")
+    if method == "dma" and block_mapping.device.type != "cpu":
+        raise ValueError("method 'dma' reads block_mapping on the host: pass a CPU tensor")
+    for t, n in ((src_key, "src_key"), (src_value, "src_value"), (dst_key, "dst_key"),
+                 (dst_value, "dst_value")):
+        _pool_tensor(t, n)
+    if method == "kernel":
+        _pool_tensor(block_mapping, "block_mapping")
+    elif not block_mapping.is_contiguous():
+        raise ValueError("block_mapping must be contiguous")
+    dt = _dtype_code(src_key, src_value, dst_key, dst_value)
+    _expect(block_mapping, torch.int32, 2, "block_mapping")
+    if block_mapping.shape[0] and block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2]")
+    if src_key.dim() != 4 or src_value.shape != src_key.shape or dst_value.shape != dst_key.shape:
+        raise ValueError("pools [NB,bs,H,D] expected, K and V alike")
+    NBs, bs, H, D = src_key.shape
+    NBd, bs2, H2, D2 = dst_key.shape
+    if (bs2, H2, D2) != (bs, H, D):
+        raise ValueError("source and destination pools disagree in block_size, heads or head_dim")
+    gpus = {t.device for t in (src_key, src_value, dst_key, dst_value, block_mapping)
+            if t.device.type == "cuda"}
+    if len(gpus) != 1:
+        raise ValueError("exactly one GPU must be involved")
+    dev = next(iter(gpus))
+    fn = "swap_blocks" if method == "kernel" else "swap_blocks_dma"
+    rc = getattr(lib(), fn)(src_key.data_ptr(), src_value.data_ptr(), dst_key.data_ptr(),
+                            dst_value.data_ptr(), block_mapping.data_ptr(),
+                            block_mapping.shape[0], H, D, NBs, NBd, bs, dt,
+                            torch.cuda.current_stream(dev).cuda_stream)
+    check(fn, rc)

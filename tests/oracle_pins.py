@@ -75,7 +75,8 @@ def paged_case(seed, ctxs, H, D, dtype, extra_blocks=3, bs=16):
     mb = max((c + bs - 1) // bs for c in ctxs)
     tables = alloc.tables_array(list(range(len(ctxs))), mb)
     return dict(q=q, kc=kc.reshape(nb, bs, H, D), vc=vc.reshape(nb, bs, H, D), tables=tables,
-                ctx=np.array(ctxs, np.int32), Ks=Ks, Vs=Vs, bs=bs, dtype=dtype, H=H, D=D)
+                ctx=np.array(ctxs, np.int32), Ks=Ks, Vs=Vs, bs=bs, dtype=dtype, H=H, D=D,
+                alloc=alloc)
 
 
 # --------------------------------------------------------------------------- pins
@@ -258,6 +259,45 @@ def pin_copy_blocks(co):
         assert np.array_equal(K2[b], kc[b]) and np.array_equal(V2[b], vc[b])
 
 
+def pin_swap_blocks(co):
+    """Swap a sequence out to a host pool, let its freed device blocks be
+    overwritten, swap it back into whatever blocks the allocator gives: its
+    attention through the new table is bit-identical to before; the host
+    blocks not written keep their bits; source pools are never changed."""
+    from oracle import paged_attention as pa
+    from workloads import SwapSpace
+    for bs in (8, 16):
+        c = paged_case(41 + bs, [20, 33, 50, 7], 2, 64, "f16", extra_blocks=6, bs=bs)
+        alloc, kc, vc = c["alloc"], c["kc"], c["vc"]
+        rng = np.random.default_rng(bs)
+        sw = SwapSpace(alloc, 16, free_order=rng.permutation(16))
+        before = pa.paged_attention_decode(c["q"], kc, vc, c["tables"], c["ctx"], 0.125, bs, "f16")
+        hk = rng.integers(0, 1 << 16, size=(16, bs, 2, 64), dtype=np.uint16)
+        hv = rng.integers(0, 1 << 16, size=(16, bs, 2, 64), dtype=np.uint16)
+        kc0, vc0, hk0, hv0 = kc.copy(), vc.copy(), hk.copy(), hv.copy()
+        out_pairs = sw.swap_out(1)
+        HK, HV = co.swap_blocks(kc, vc, hk, hv, out_pairs)
+        assert np.array_equal(kc, kc0) and np.array_equal(vc, vc0)      # source untouched
+        held = set(out_pairs[:, 1].tolist())
+        for b in range(16):
+            if b not in held:
+                assert np.array_equal(HK[b], hk0[b]) and np.array_equal(HV[b], hv0[b])
+        kc2, vc2 = kc.copy(), vc.copy()
+        for b in alloc.free_blocks():                                    # reuse overwrites them
+            kc2[b] = rng.integers(0, 1 << 16, size=kc2[b].shape, dtype=np.uint16)
+            vc2[b] = rng.integers(0, 1 << 16, size=vc2[b].shape, dtype=np.uint16)
+        in_pairs = sw.swap_in(1)
+        assert set(in_pairs[:, 1].tolist()) != set(out_pairs[:, 0].tolist())  # other blocks
+        K3, V3 = co.swap_blocks(HK, HV, kc2, vc2, in_pairs)
+        tables = alloc.tables_array(list(range(4)), c["tables"].shape[1])
+        after = pa.paged_attention_decode(c["q"], K3, V3, tables, c["ctx"], 0.125, bs, "f16")
+        assert np.array_equal(before, after)
+        dst = set(in_pairs[:, 1].tolist())
+        for b in range(kc.shape[0]):
+            if b not in dst:
+                assert np.array_equal(K3[b], kc2[b]) and np.array_equal(V3[b], vc2[b])
+
+
 ATTENTION_PINS = [pin_translate, pin_upcast, pin_sdpa, pin_bruteforce, pin_contiguous,
                   pin_permutation, pin_one_token, pin_weights_sum, pin_partitioned]
-CACHE_PINS = [pin_reshape_and_cache, pin_copy_blocks]
+CACHE_PINS = [pin_reshape_and_cache, pin_copy_blocks, pin_swap_blocks]

@@ -6,7 +6,7 @@ import os
 import numpy as np
 import pytest
 
-from workloads import BlockAllocator, make_config
+from workloads import BlockAllocator, SwapSpace, make_config
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -162,3 +162,93 @@ def test_shared_prefix_refcounts():
         a.free(s)
     assert a.num_free == a.num_blocks
     a.check_invariants()
+
+
+def test_p1_swap_demo_counts():
+    d = _demos()["p1_swap_demo"]
+    bs = d["block_size"]
+    a = BlockAllocator(d["num_blocks"], bs)
+    a.allocate(1, d["req1_blocks"] * bs)
+    a.allocate(2, d["req2_blocks"] * bs)
+    assert a.num_free == d["free_before_swap"]
+    sw = SwapSpace(a, d["host_blocks"])
+    pairs = sw.swap_out(1)
+    assert pairs.shape == (d["req1_blocks"], 2)
+    assert a.num_free == d["free_after_swap_out"]
+    assert sw.num_free == d["host_free_after_swap_out"]
+    assert (a.num_free >= d["req3_blocks_in_demo"]) == d["req3_fits"]
+    with pytest.raises(MemoryError):
+        a.allocate(3, d["req3_blocks_in_demo"] * bs)
+    a.allocate(3, a.num_free * bs)                      # what does fit
+    with pytest.raises(MemoryError):                    # no device room to swap back in
+        sw.swap_in(1)
+    assert sw.swapped() == [1] and sw.num_free == d["host_free_after_swap_out"]
+    a.free(3)
+    back = sw.swap_in(1)
+    assert back.shape == (d["req1_blocks"], 2)
+    assert list(back[:, 0]) == list(pairs[:, 1])        # the same host blocks, in order
+    assert a.num_free == d["free_before_swap"] and sw.num_free == d["host_blocks"]
+    a.check_invariants()
+    sw.check_invariants()
+
+
+def test_swap_space_random_operations_keep_invariants():
+    rng = np.random.default_rng(7)
+    a = BlockAllocator(64, 16, free_order=rng.permutation(64))
+    sw = SwapSpace(a, 48, free_order=rng.permutation(48))
+    live, out = set(), set()
+    for step in range(400):
+        op = rng.integers(0, 5)
+        try:
+            if op == 0:
+                s = int(step)
+                a.allocate(s, int(rng.integers(1, 80)))
+                live.add(s)
+            elif op == 1 and live:
+                s = int(rng.choice(sorted(live)))
+                a.append_tokens(s, int(rng.integers(1, 20)))
+            elif op == 2 and live:
+                s = int(rng.choice(sorted(live)))
+                table, tokens = a.block_table(s), a.num_tokens(s)
+                pairs = sw.swap_out(s)
+                assert list(pairs[:, 0]) == table and sw.host_table(s) == list(pairs[:, 1])
+                live.discard(s)
+                out.add(s)
+                assert len(sw.host_table(s)) == len(table)
+                assert tokens == (sw._swapped[s][1])
+            elif op == 3 and out:
+                s = int(rng.choice(sorted(out)))
+                host = sw.host_table(s)
+                pairs = sw.swap_in(s)
+                assert list(pairs[:, 0]) == host and list(pairs[:, 1]) == a.block_table(s)
+                out.discard(s)
+                live.add(s)
+            elif op == 4 and live:
+                s = int(rng.choice(sorted(live)))
+                a.free(s)
+                live.discard(s)
+        except MemoryError:
+            pass
+        a.check_invariants()
+        sw.check_invariants()
+        assert set(a.sequences()) == live and set(sw.swapped()) == out
+
+
+def test_swap_out_of_a_shared_prefix_keeps_the_other_readers():
+    a = BlockAllocator(16, 16)
+    a.allocate("p", 40)                                  # 3 blocks
+    a.fork("p", "q")
+    sw = SwapSpace(a, 8)
+    pairs = sw.swap_out("q")
+    assert list(pairs[:, 0]) == a.block_table("p")       # the shared blocks are copied
+    assert all(a.refcount(b) == 1 for b in a.block_table("p"))
+    assert a.num_free == 13                              # nothing freed: "p" still maps them
+    back = sw.swap_in("q")
+    assert not set(back[:, 1]) & set(a.block_table("p"))  # private copies now
+    sw.swap_out("p")
+    with pytest.raises(ValueError):                      # already swapped out
+        sw.swap_out("p")
+    with pytest.raises(KeyError):
+        sw.swap_in("nobody")
+    a.check_invariants()
+    sw.check_invariants()

@@ -188,7 +188,25 @@ def _copy_key_only(kc, vc, pairs):
     return K, vc.copy()
 
 
+def _swap_reversed(sk, sv, dk, dv, pairs):
+    K, V = dk.copy(), dv.copy()
+    for s, d in np.asarray(pairs).tolist():
+        if s < K.shape[0] and d < sk.shape[0]:
+            K[s] = sk[d]
+            V[s] = sv[d]
+    return K, V
+
+
+def _swap_key_only(sk, sv, dk, dv, pairs):
+    K = dk.copy()
+    for s, d in np.asarray(pairs).tolist():
+        K[d] = sk[s]
+    return K, dv.copy()
+
+
 CACHE_MUTANTS = {
+    "swap_reversed": ("swap_blocks", _swap_reversed),
+    "swap_key_only": ("swap_blocks", _swap_key_only),
     "write_swapped": ("reshape_and_cache", _write_swapped),
     "write_drops_value": ("reshape_and_cache", _write_drops_value),
     "copy_reversed": ("copy_blocks", _copy_reversed),
@@ -200,4 +218,5 @@ CACHE_MUTANTS = {
 def test_pins_catch_planted_cache_mistake(name, monkeypatch):
     attr, fn = CACHE_MUTANTS[name]
     monkeypatch.setattr(co, attr, fn)
-    assert _fails_some_pin(CACHE_PINS, co), f"no pin caught mutant {name}"
+    with np.errstate(all="ignore"):                 # a mutant may leave NaN canaries in play
+        assert _fails_some_pin(CACHE_PINS, co), f"no pin caught mutant {name}"

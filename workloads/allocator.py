@@ -213,3 +213,82 @@ class BlockAllocator:
                 counts[b] += 1
         if counts != self._ref:
             raise AssertionError("reference counts disagree with the block tables")
+
+
+class SwapSpace:
+    """Host swap space for one device pool: a pool of host blocks with its own
+    free list, and the sequences that are swapped out.
+
+    [P1 §3.3.3 "显存不足时的处理策略", CPU Swap and its SwapManager simulation:
+    swapping a sequence out copies each block of its table into a host block
+    taken from a pre-allocated host pool and frees its device blocks; swapping
+    it in takes device blocks again (any free ones) and copies the data back,
+    returning the host blocks.] ``swap_out`` and ``swap_in`` return the
+    (src, dst) block pairs of the copy; the caller moves the data with one
+    ``swap_blocks`` launch, issued on the stream before any later write to a
+    block freed here.
+
+    Readings where the pages are silent: a device block the sequence shares
+    with others only loses this sequence's reference (the others keep it);
+    the copy it gets back on swap-in is private. Out of host blocks on
+    swap-out, or of device blocks on swap-in: ``MemoryError``, nothing changed.
+    """
+
+    def __init__(self, device: BlockAllocator, num_host_blocks: int, free_order=None):
+        if num_host_blocks <= 0:
+            raise ValueError("num_host_blocks must be positive")
+        self.device = device
+        self.num_blocks = int(num_host_blocks)
+        order = list(range(num_host_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_host_blocks)):
+            raise ValueError("free_order must be a permutation of range(num_host_blocks)")
+        self._free = deque(order)
+        self._swapped: dict = {}     # seq -> (host blocks in logical order, token count)
+
+    @property
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def swapped(self) -> list:
+        return list(self._swapped)
+
+    def host_table(self, seq) -> list:
+        return list(self._swapped[seq][0])
+
+    def swap_out(self, seq) -> np.ndarray:
+        """Move ``seq`` to host blocks; returns int32 [n, 2] (device, host) pairs
+        in logical-block order."""
+        if seq in self._swapped:
+            raise ValueError(f"sequence {seq!r} is already swapped out")
+        table = self.device.block_table(seq)           # KeyError if unknown
+        tokens = self.device.num_tokens(seq)
+        if len(table) > len(self._free):
+            raise MemoryError(f"out of host swap blocks: need {len(table)}, {len(self._free)} free")
+        host = [self._free.popleft() for _ in table]
+        self.device.free(seq)
+        self._swapped[seq] = (host, tokens)
+        return np.asarray(list(zip(table, host)), dtype=np.int32).reshape(-1, 2)
+
+    def swap_in(self, seq) -> np.ndarray:
+        """Bring ``seq`` back into newly allocated device blocks; returns int32
+        [n, 2] (host, device) pairs in logical-block order."""
+        host, tokens = self._swapped[seq]                # KeyError if not swapped out
+        if len(host) > self.device.num_free:
+            raise MemoryError(f"out of device blocks: need {len(host)}, "
+                              f"{self.device.num_free} free")
+        table = self.device.allocate(seq, tokens)
+        if len(table) != len(host):
+            raise AssertionError("a swapped sequence's token count no longer fits its blocks")
+        del self._swapped[seq]
+        self._free.extend(host)
+        return np.asarray(list(zip(host, table)), dtype=np.int32).reshape(-1, 2)
+
+    def check_invariants(self) -> None:
+        held = [b for host, _ in self._swapped.values() for b in host]
+        free = list(self._free)
+        if len(set(held)) != len(held) or set(held) & set(free):
+            raise AssertionError("a host block is held twice or held and free")
+        if len(held) + len(free) != self.num_blocks:
+            raise AssertionError("held + free != host pool size")
+        if set(self._swapped) & set(self.device.sequences()):
+            raise AssertionError("a sequence is both resident and swapped out")
