@@ -67,6 +67,10 @@ def parse():
                          "swapped out to pinned host pools and back (one launch each way), "
                          "next to a contiguous pinned copy of the same bytes; prints its own "
                          "JSON line")
+    ap.add_argument("--beam", action="store_true",
+                    help="measure beam-search decoding instead: 16 prompts x 8 beams at the "
+                         "LLaMA-7B shape, 32 steps of CoW copy + cache write + decode (grouped "
+                         "by prompt, grouped by parent, and plain); prints its own JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -314,6 +318,89 @@ def swap_bench(args, w, dw, dev):
     print(json.dumps(res), flush=True)
 
 
+def unique_rows(tables, ctx, bs, num_blocks):
+    """Distinct (physical block, row) slots a decode over these tables reads."""
+    rows = np.zeros(num_blocks, dtype=np.int64)
+    for s in range(tables.shape[0]):
+        n = (int(ctx[s]) + bs - 1) // bs
+        r = np.minimum(bs, int(ctx[s]) - bs * np.arange(n))
+        np.maximum.at(rows, tables[s, :n].astype(np.int64), r)
+    return int(rows.sum())
+
+
+def beam_bench(args, dev):
+    """Beam search over 32 steps: every step's inputs are built on the host and
+    uploaded first; then each step (CoW copies, cache write, decode) is timed
+    with HIP events. Three decode variants on identical inputs."""
+    import torch
+
+    import paged_kv_cache_159_amd as pkv
+    from workloads import BeamSearch
+    from workloads.device import bits_to_device
+
+    steps = 32
+    res = {"metric": "beam-search decode step, unique KV GB/s", "unit": "GB/s", "data": "synthetic"}
+    for mode in ("prompt", "parent", "plain"):
+        b = BeamSearch(prompts=16, beams=8, steps=steps, dtype="f16", block_size=args.block_size,
+                       seed=7, groups="prompt" if mode == "plain" else mode)
+        kc = bits_to_device(b.key_cache, b.dtype, dev)
+        vc = bits_to_device(b.value_cache, b.dtype, dev)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        plan, ubytes, saving, shared = [], 0, [], []
+        kvt = 2 * b.H * b.D * 2
+        for _ in range(steps):
+            st = b.step()
+            plan.append(dict(pairs=up(st.copy_pairs), nk=bits_to_device(st.new_key, b.dtype, dev),
+                             nv=bits_to_device(st.new_value, b.dtype, dev), slots=up(st.slot_mapping),
+                             q=bits_to_device(st.query, b.dtype, dev), bt=up(st.block_tables),
+                             ctx=up(st.context_lens), gs=up(st.group_start), sb=up(st.shared_blocks)))
+            ubytes += unique_rows(st.block_tables, st.context_lens, b.bs, b.num_blocks) * kvt
+            saving.append(1 - st.blocks_in_use / st.blocks_unshared)
+            shared.append(float(np.mean(st.shared_blocks)))
+        out = torch.empty_like(plan[0]["q"])
+        gws = torch.empty(max(pkv.grouped_workspace_size(b.num_seqs, b.H, b.D, b.max_blocks, b.bs), 16),
+                          dtype=torch.uint8, device=dev)
+        ws = pkv.alloc_workspace(b.num_seqs, b.H, b.D, b.max_blocks, b.bs, device=dev)
+
+        def run(record):
+            evs = []
+            for p in plan:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e2 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if p["pairs"].shape[0]:
+                    pkv.copy_blocks(kc, vc, p["pairs"])
+                pkv.reshape_and_cache(p["nk"], p["nv"], kc, vc, p["slots"])
+                e1.record()
+                if mode == "plain":
+                    pkv.paged_attention_decode(out, p["q"], kc, vc, p["bt"], p["ctx"], b.scale,
+                                               workspace=ws)
+                else:
+                    pkv.paged_attention_decode_grouped(out, p["q"], kc, vc, p["bt"], p["ctx"],
+                                                       p["gs"], p["sb"], b.scale, workspace=gws)
+                e2.record()
+                evs.append((e0, e1, e2))
+            torch.cuda.synchronize()
+            return evs
+
+        run(False)
+        evs = run(True)
+        step_us = float(np.sum([a.elapsed_time(c) for a, _, c in evs])) * 1e3 / steps
+        dec_us = float(np.sum([b_.elapsed_time(c) for _, b_, c in evs])) * 1e3 / steps
+        res[mode] = {"step_us": round(step_us, 2), "decode_us": round(dec_us, 2),
+                     "decode_unique_gbs": round(ubytes / steps / (dec_us * 1e-6) / 1e9, 1)}
+        res["memory_saving_by_sharing"] = round(float(np.mean(saving)), 4)
+        if mode != "plain":
+            res[mode]["mean_shared_blocks_per_group"] = round(float(np.mean(shared)), 2)
+        del kc, vc, plan
+        torch.cuda.empty_cache()
+    res["value"] = res["prompt"]["decode_unique_gbs"]
+    res["config"] = {"workload": f"beam search: 16 prompts x 8 beams, prompts 256..1024 tokens, "
+                                 f"32 steps, 32 heads x 128, f16, block_size {args.block_size}"}
+    print(json.dumps(res), flush=True)
+
+
 def load_traffic(key):
     """HBM traffic per decode launch from committed rocprofv3 counter runs,
     only if they were taken on the current decode kernel source."""
@@ -373,6 +460,11 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.beam:
+        import torch
+        torch.cuda.set_device(0)
+        beam_bench(args, torch.device("cuda", 0))
         return
     if args.traffic_summary:
         sys.path.insert(0, ROOT)

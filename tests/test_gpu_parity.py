@@ -529,3 +529,63 @@ def test_swap_rejects_bad_memory():
     assert rc == 0
     torch.cuda.synchronize()
     del ctypes
+
+
+# ------------------------------------------------------------ beam search over many steps
+
+def _run_beam(b, steps, check_every=1):
+    """Drive ``steps`` beam-search steps on the GPU and on the oracle from the
+    same step inputs; after every ``check_every`` steps: pools bit-exact, the
+    grouped decode within the bar against the oracle and close to the plain
+    decode."""
+    from workloads.device import bits_to_device
+    pkv = _pkv()
+    kc = bits_to_device(b.key_cache, b.dtype)
+    vc = bits_to_device(b.value_cache, b.dtype)
+    K, V = b.key_cache, b.value_cache
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    for t in range(steps):
+        st = b.step()
+        if len(st.copy_pairs):
+            pkv.copy_blocks(kc, vc, dev(st.copy_pairs))
+        pkv.reshape_and_cache(bits_to_device(st.new_key, b.dtype), bits_to_device(st.new_value, b.dtype),
+                              kc, vc, dev(st.slot_mapping))
+        q = bits_to_device(st.query, b.dtype)
+        out = torch.empty_like(q)
+        tables, ctx = dev(st.block_tables), dev(st.context_lens)
+        pkv.paged_attention_decode_grouped(out, q, kc, vc, tables, ctx, dev(st.group_start),
+                                           dev(st.shared_blocks), b.scale)
+        K, V = oracle.copy_blocks(K, V, st.copy_pairs) if len(st.copy_pairs) else (K, V)
+        K, V = oracle.reshape_and_cache(st.new_key, st.new_value, K, V, st.slot_mapping, b.bs)
+        if (t + 1) % check_every and t + 1 != steps:
+            continue
+        plain = torch.empty_like(q)
+        pkv.paged_attention_decode(plain, q, kc, vc, tables, ctx, b.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(device_to_bits(kc), K), f"key pool differs after step {t}"
+        assert np.array_equal(device_to_bits(vc), V), f"value pool differs after step {t}"
+        want = oracle.paged_attention_decode(st.query, K, V, st.block_tables, st.context_lens,
+                                             b.scale, b.bs, b.dtype)
+        say(f"beam step {t}: ctx {int(st.context_lens[0])} pairs {len(st.copy_pairs)} "
+            f"groups {len(st.shared_blocks)} shared {st.shared_blocks[:4].tolist()}")
+        assert_attention_close(device_to_float64(out), want, what=f"beam step {t}")
+        diff = np.abs(device_to_float64(out) - device_to_float64(plain))
+        assert diff.max() <= MAX_ABS
+
+
+@pytest.mark.parametrize("groups,bs", [("prompt", 16), ("parent", 16), ("parent", 8), ("prompt", 32)])
+def test_beam_search_many_steps(groups, bs):
+    """3 prompts x 4 beams, 40 steps of fork / free / CoW / grouped decode with
+    groups re-formed every step."""
+    from workloads import BeamSearch
+    b = BeamSearch(prompts=3, beams=4, prompt_lo=20, prompt_hi=70, steps=40, num_heads=4,
+                   head_dim=64, dtype="f16", block_size=bs, seed=17, groups=groups)
+    _run_beam(b, 40)
+
+
+def test_beam_search_llama_shape():
+    """16 prompts x 8 beams at the LLaMA-7B shape, bf16, prompts of 256..1024
+    tokens, 3 steps."""
+    from workloads import BeamSearch
+    b = BeamSearch(prompts=16, beams=8, steps=3, dtype="bf16", seed=5, groups="prompt")
+    _run_beam(b, 3)
