@@ -1,4 +1,4 @@
-"""CPU oracle for paged decode attention, the slot-mapped cache write and the CoW block copy.
+"""CPU oracle for paged decode and prefill attention, the slot-mapped cache write, the CoW block copy and block swap.
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this package.
@@ -39,3 +39,4 @@ from .paged_attention import (  # noqa: F401
     merge_partitions,
 )
 from .cache_ops import reshape_and_cache, copy_blocks, swap_blocks  # noqa: F401
+from .prefill import causal_attention, paged_attention_prefill  # noqa: F401

@@ -301,3 +301,94 @@ def pin_swap_blocks(co):
 ATTENTION_PINS = [pin_translate, pin_upcast, pin_sdpa, pin_bruteforce, pin_contiguous,
                   pin_permutation, pin_one_token, pin_weights_sum, pin_partitioned]
 CACHE_PINS = [pin_reshape_and_cache, pin_copy_blocks, pin_swap_blocks]
+
+
+# --------------------------------------------------------------------------- prefill pins
+
+def _prefill_case(seed, ctxs, qlens, H, D, dtype, bs=16):
+    """paged_case plus packed chunk queries: sequence s asks for its last
+    qlens[s] tokens."""
+    c = paged_case(seed, ctxs, H, D, dtype, bs=bs)
+    rng = np.random.default_rng(seed + 100)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int64)
+    c["Q"] = _rand_bits(rng, (int(qs[-1]), H, D), dtype)
+    c["qs"] = qs
+    return c
+
+
+def _sdpa_masked(Q, K, V, scale, first_pos):
+    q = torch.from_numpy(Q)[None, None]
+    k = torch.from_numpy(K)[None, None]
+    v = torch.from_numpy(V)[None, None]
+    n, ctx = Q.shape[0], K.shape[0]
+    if first_pos == 0 and n == ctx:
+        out = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+    else:                             # bottom-right aligned: query i sits at first_pos + i
+        mask = torch.arange(ctx)[None, :] <= (first_pos + torch.arange(n))[:, None]
+        out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return out[0, 0].numpy()
+
+
+def pin_prefill_sdpa(pf):
+    """Whole prompts (q_len = ctx) equal torch's causal scaled_dot_product_attention
+    over the contiguous rows, and chunks (q_len < ctx) equal it with the
+    bottom-right causal mask; rows placed through the allocator's slots with
+    NaN everywhere else, at block sizes 16 and 8."""
+    for bs, ctxs, qlens in ((16, [1, 17, 40, 70], [1, 17, 40, 70]), (16, [33, 70, 5], [8, 1, 5]),
+                            (8, [9, 31, 64], [9, 16, 3])):
+        c = _prefill_case(61 + bs + len(ctxs), ctxs, qlens, 2, 64, "f16", bs=bs)
+        scale = 0.125
+        out = pf.paged_attention_prefill(c["Q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qs"],
+                                         scale, bs, "f16")
+        assert np.isfinite(out).all()
+        for s, (ctx, n) in enumerate(zip(ctxs, qlens)):
+            K = _torch_upcast(c["Ks"][s], "f16")
+            V = _torch_upcast(c["Vs"][s], "f16")
+            Q = _torch_upcast(c["Q"][c["qs"][s]:c["qs"][s + 1]], "f16")
+            for h in range(2):
+                want = _sdpa_masked(Q[:, h], K[:, h], V[:, h], scale, ctx - n)
+                got = out[c["qs"][s]:c["qs"][s + 1], h]
+                assert np.allclose(got, want, rtol=0, atol=1e-12), (bs, s, h)
+
+
+def pin_prefill_decode(pf):
+    """One query per sequence (q_len = 1) is the decode of the pinned decode
+    oracle."""
+    from oracle import paged_attention as pa
+    c = _prefill_case(71, [1, 15, 16, 17, 40], [1] * 5, 3, 64, "bf16")
+    got = pf.paged_attention_prefill(c["Q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qs"],
+                                     0.2, 16, "bf16")
+    want = pa.paged_attention_decode(c["Q"], c["kc"], c["vc"], c["tables"], c["ctx"], 0.2, 16, "bf16")
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def pin_prefill_bruteforce(pf):
+    """A 6-token prompt, pure-Python loops and math.exp, causal by hand."""
+    c = _prefill_case(72, [6], [6], 1, 4, "f16")
+    out = pf.paged_attention_prefill(c["Q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qs"],
+                                     0.5, 16, "f16")
+    K = _torch_upcast(c["Ks"][0], "f16")[:, 0].tolist()
+    V = _torch_upcast(c["Vs"][0], "f16")[:, 0].tolist()
+    Q = _torch_upcast(c["Q"], "f16")[:, 0].tolist()
+    for i in range(6):
+        xs = [0.5 * sum(Q[i][d] * K[j][d] for d in range(4)) for j in range(i + 1)]
+        m = max(xs)
+        ws = [math.exp(x - m) for x in xs]
+        z = sum(ws)
+        for d in range(4):
+            want = sum(ws[j] * V[j][d] for j in range(i + 1)) / z
+            assert abs(out[i, 0, d] - want) <= 1e-12
+
+
+def pin_prefill_chunks(pf):
+    """Chunks see the cached prefix: the last 20 queries of a 50-token prompt
+    asked as one chunk equal the same rows of the whole-prompt call."""
+    c = _prefill_case(73, [50], [50], 2, 64, "f16")
+    whole = pf.paged_attention_prefill(c["Q"], c["kc"], c["vc"], c["tables"], c["ctx"], c["qs"],
+                                       0.125, 16, "f16")
+    tail = pf.paged_attention_prefill(c["Q"][30:], c["kc"], c["vc"], c["tables"], c["ctx"],
+                                      np.array([0, 20]), 0.125, 16, "f16")
+    assert np.allclose(tail, whole[30:], rtol=0, atol=1e-12)
+
+
+PREFILL_PINS = [pin_prefill_sdpa, pin_prefill_decode, pin_prefill_bruteforce, pin_prefill_chunks]

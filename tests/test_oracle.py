@@ -220,3 +220,75 @@ def test_pins_catch_planted_cache_mistake(name, monkeypatch):
     monkeypatch.setattr(co, attr, fn)
     with np.errstate(all="ignore"):                 # a mutant may leave NaN canaries in play
         assert _fails_some_pin(CACHE_PINS, co), f"no pin caught mutant {name}"
+
+
+# --------------------------------------------------------------------------- prefill
+
+from oracle import prefill as pf  # noqa: E402
+from oracle_pins import PREFILL_PINS  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", PREFILL_PINS, ids=lambda f: f.__name__)
+def test_prefill_pin(pin):
+    pin(pf)
+
+
+def test_prefill_refuses_bad_chunks():
+    kc = np.zeros((2, 16, 1, 8), np.uint16)
+    q = np.zeros((5, 1, 8), np.uint16)
+    with pytest.raises(ValueError):                       # chunk longer than the context
+        oracle.paged_attention_prefill(q, kc, kc, [[0, 1]], [4], [0, 5], 1.0, 16, "f16")
+    with pytest.raises(ValueError):                       # query_start must cover the rows
+        oracle.paged_attention_prefill(q, kc, kc, [[0, 1]], [8], [0, 4], 1.0, 16, "f16")
+
+
+def _mask(ctx, n, first_pos, strict=False):
+    pos = first_pos + np.arange(n)[:, None]
+    j = np.arange(ctx)[None, :]
+    return (j < pos) if strict else (j <= pos)
+
+
+def _softmax_rows(X):
+    W = np.exp(X - X.max(axis=1, keepdims=True))
+    return W / W.sum(axis=1, keepdims=True)
+
+
+def _ca_no_mask(Q, K, V, scale, first_pos):
+    return _softmax_rows(scale * (Q @ K.T)) @ V
+
+
+def _ca_no_diagonal(Q, K, V, scale, first_pos):
+    X = np.where(_mask(K.shape[0], Q.shape[0], first_pos, strict=True), scale * (Q @ K.T), -np.inf)
+    X[:, 0] = np.where(np.isinf(X[:, 0]), 0.0, X[:, 0])     # keep rows finite
+    return _softmax_rows(X) @ V
+
+
+def _ca_top_left(Q, K, V, scale, first_pos):
+    X = np.where(_mask(K.shape[0], Q.shape[0], 0), scale * (Q @ K.T), -np.inf)
+    return _softmax_rows(X) @ V
+
+
+def _ca_no_scale(Q, K, V, scale, first_pos):
+    X = np.where(_mask(K.shape[0], Q.shape[0], first_pos), Q @ K.T, -np.inf)
+    return _softmax_rows(X) @ V
+
+
+def _ca_k_for_v(Q, K, V, scale, first_pos):
+    X = np.where(_mask(K.shape[0], Q.shape[0], first_pos), scale * (Q @ K.T), -np.inf)
+    return _softmax_rows(X) @ K
+
+
+PREFILL_MUTANTS = {
+    "no_causal_mask": _ca_no_mask,
+    "mask_drops_diagonal": _ca_no_diagonal,
+    "mask_top_left_aligned": _ca_top_left,
+    "scale_dropped": _ca_no_scale,
+    "keys_for_values": _ca_k_for_v,
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_pins_catch_planted_prefill_mistake(name, monkeypatch):
+    monkeypatch.setattr(pf, "causal_attention", PREFILL_MUTANTS[name])
+    with np.errstate(all="ignore"):
+        assert _fails_some_pin(PREFILL_PINS, pf), f"no pin caught mutant {name}"
