@@ -188,6 +188,34 @@ int paged_attention_decode_grouped(void* out, const void* query,
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-token (prefill / chunked-prefill) attention over the paged cache, on
+ * the MFMA matrix cores [P1 §3.3.2 "动态页面分配机制": a prompt's pages are
+ * allocated in one go at prefill; P3 §3.1.3: the same address translation as
+ * decode]. The pages give no formula; the reading is causal scaled
+ * dot-product attention. Sequence s's query rows are
+ * query[query_start[s] .. query_start[s+1]) ([rows][num_heads][head_dim], the
+ * same layout for `out`): its last q_len = query_start[s+1] - query_start[s]
+ * tokens, at positions context_lens[s] - q_len .. context_lens[s] - 1, whose
+ * K/V must already be in the cache (reshape_and_cache first). Query i attends
+ * over tokens 0 .. context_lens[s] - q_len + i of its sequence. q_len =
+ * context_lens[s] is a whole prompt, a smaller q_len a chunk after a cached
+ * prefix, q_len = 0 skips the sequence.
+ *   query_start  int32 [num_seqs + 1], device: 0, nondecreasing; the rows of
+ *                query and out are query_start[num_seqs].
+ *   max_query_len  host bound on every q_len (sizes the grid; rows of a longer
+ *                chunk beyond it are not computed). <= max_blocks_per_seq *
+ *                block_size.
+ * Preconditions as for decode, plus q_len <= context_lens[s]. No workspace;
+ * one launch on `stream`; output rounded to nearest even from fp32.
+ */
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start,
+                            int num_seqs, int max_query_len, int num_heads, int head_dim,
+                            int num_blocks, int block_size, int max_blocks_per_seq, float scale,
+                            int dtype, void* stream);
+
+/*
  * Slot-mapped cache write [P2 "Copy-on-Write共享解码的显存优化原理": the new
  * token's K/V is written into its block; P1 §3.3.2 "动态页面分配机制"]. For each
  * token i with slot_mapping[i] >= 0:

@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     paged_attention_decode_grouped,
     paged_attention_decode_merge,
     paged_attention_decode_partitions,
+    paged_attention_prefill,
     reshape_and_cache,
     swap_blocks,
     workspace_size,

@@ -23,6 +23,7 @@ EXPORTS = (
     "paged_attention_decode_merge",
     "paged_attention_grouped_workspace_size",
     "paged_attention_decode_grouped",
+    "paged_attention_prefill",
     "reshape_and_cache",
     "copy_blocks",
     "swap_blocks",
@@ -51,6 +52,8 @@ _SIGNATURES = {
     "paged_attention_grouped_workspace_size": (_z, [_i, _i, _i, _i, _i]),
     "paged_attention_decode_grouped": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                                             _f, _i, _p, _z, _p]),
+    "paged_attention_prefill": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f,
+                                     _i, _p]),
     "reshape_and_cache": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "copy_blocks": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "swap_blocks": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),

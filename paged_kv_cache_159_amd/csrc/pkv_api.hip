@@ -350,6 +350,48 @@ int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping
                                            static_cast<hipStream_t>(stream)));
 }
 
+int paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start,
+                            int num_seqs, int max_query_len, int num_heads, int head_dim,
+                            int num_blocks, int block_size, int max_blocks_per_seq, float scale,
+                            int dtype, void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, num_blocks);
+  if (rc) return rc;
+  if (num_seqs < 0 || max_query_len < 0 || max_blocks_per_seq < 1) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxGrid) return PKV_ERR_SHAPE;
+  if (max_query_len > max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+  if (num_seqs > 65535) return PKV_ERR_SHAPE;  // grid y
+  const int64_t tiles = (max_query_len + pkv::prefill_rows_per_tile() - 1) /
+                        pkv::prefill_rows_per_tile();
+  if (tiles * num_heads > kMaxGrid) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !query_start)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start))
+    return PKV_ERR_ALIGN;
+  pkv::PrefillArgs a = {};
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_size;
+  a.max_query_len = max_query_len;
+  a.scale = scale;
+  a.dtype = dtype;
+  return status_of(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 int swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
                 const int32_t* block_mapping, int num_pairs, int num_heads, int head_dim,
                 int src_num_blocks, int dst_num_blocks, int block_size, int dtype, void* stream) {

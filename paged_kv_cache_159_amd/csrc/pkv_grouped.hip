@@ -31,43 +31,10 @@
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_mfma.h"
 #include "pkv_partition.h"
 
 namespace pkv {
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-typedef short s4_t __attribute__((ext_vector_type(4)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-template <typename T> struct Mfma;
-
-template <> struct Mfma<F16> {
-  static __device__ __forceinline__ f4_t qk(uint4 a, uint4 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
-                                                  __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f4_t pv(uint2 a, uint2 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a),
-                                                 __builtin_bit_cast(h4_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ float widen(uint32_t x) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)x);
-  }
-};
-
-template <> struct Mfma<BF16> {
-  static __device__ __forceinline__ f4_t qk(uint4 a, uint4 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a),
-                                                   __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f4_t pv(uint2 a, uint2 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a),
-                                                     __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ float widen(uint32_t x) { return __uint_as_float(x << 16); }
-};
 
 constexpr int kQueryTile = 16;
 constexpr int kGroupedWaves = 8;   // same workgroup shape as the partition kernel
@@ -164,7 +131,7 @@ __device__ __forceinline__ void shared_unit(
       for (int i = 0; i < NQK; ++i) {
         const uint4 kf =
             *reinterpret_cast<const uint4*>(s_k + col * ROW + (grp * SPAN + 8 * i) * 2);
-        sacc = M::qk(kf, qf[i], sacc);
+        sacc = M::k32(kf, qf[i], sacc);
       }
       // sacc[v] = S^T[token 4*grp + v][query col]; shared tiles are full.
       float x[4];
@@ -201,8 +168,8 @@ __device__ __forceinline__ void shared_unit(
         const uint32_t a2 = *reinterpret_cast<const uint16_t*>(vp + 2 * ROW);
         const uint32_t a3 = *reinterpret_cast<const uint16_t*>(vp + 3 * ROW);
         const uint2 av = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-        acc = M::pv(av, bhi, acc);
-        acc = M::pv(av, blo, acc);
+        acc = M::k16(av, bhi, acc);
+        acc = M::k16(av, blo, acc);
       }
     }
     // acc[v] = O^T[dim 16*wave + 4*grp + v][query col], unnormalised

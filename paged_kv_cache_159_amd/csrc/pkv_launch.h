@@ -54,6 +54,29 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 // grid (the merge follows with launch_decode_merge).
 hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t stream);
 
+// Prefill / chunked-prefill attention (MFMA): one launch.
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;   // [num_seqs + 1] packed query rows per sequence
+  int num_seqs;
+  int num_heads;
+  int head_dim;
+  int max_blocks_per_seq;
+  int block_size;
+  int max_query_len;            // bound on query_start[s+1] - query_start[s]
+  float scale;
+  int dtype;
+};
+// Chunk rows one prefill workgroup covers (the grid has ceil(max_query_len /
+// rows) tiles per sequence and head).
+int prefill_rows_per_tile();
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int64_t* slot_mapping, int num_tokens,
                                     int row_elems, hipStream_t stream);

@@ -1,0 +1,276 @@
+// Multi-token (prefill / chunked-prefill) paged attention for gfx950 on the
+// MFMA matrix cores.
+//
+// Pages: a prompt's KV goes into pages allocated in one go at prefill ([P1]
+// "3.3 页面级显存管理" §3.3.2 "动态页面分配机制": a 320-token prompt takes 20
+// pages), read back through the block table with the same translation as
+// decode ([P3] "3.1 PagedAttention的核心原理" §3.1.3); prefix pages may be shared
+// at prefill as at decode ([P2] "Copy-on-Write共享解码的显存优化原理"). The pages
+// give no attention formula; the reading taken is causal scaled dot-product
+// attention: sequence s's chunk of q_len new tokens sits at positions
+// ctx - q_len .. ctx - 1 (its K/V already written to the cache), and query i
+// attends over tokens 0 .. ctx - q_len + i through the block table. q_len = ctx
+// is a whole prompt, q_len < ctx a chunk after a cached prefix.
+//
+// Work decomposition. One 4-wave workgroup per (sequence, tile of 128 chunk
+// rows, head); each wave owns 32 query rows as two 16-column MFMA tiles. Tiles
+// are dispatched last-first (the causal work of a tile grows with its
+// position). Keys are staged through LDS 64 at a time, gathered row by row
+// through the block table (any block size): K row-major (rows padded by 16
+// bytes), V transposed (V^T[dim][key], so an MFMA operand of 4 consecutive
+// keys of one dim is one 8-byte read). The next stage's rows are held in
+// registers while the waves compute on the current one.
+//
+// Arithmetic, per 32 keys and 16 queries:
+//   S^T = K Q^T with v_mfma_f32_16x16x32 (A = 16 key rows, B = the queries'
+//   rows), two 16-key tiles; the accumulator holds S^T[key 4g+v][query l%16].
+//   Causal mask (key position > query position -> -inf), online softmax per
+//   query column in the log2 domain (max and sum across the 4 lane groups by
+//   two shuffles).
+//   O^T += V^T P^T with one v_mfma_f32_16x16x32 per 16 output dims: its K index
+//   8g+e runs over keys 4g+e of the first tile (e < 4) and 16+4g+(e-4) of the
+//   second, which is exactly where the two S^T accumulators already hold P^T,
+//   so P never moves between lanes; V^T's operand is two 8-byte LDS reads.
+//   fp16: P is rounded once to fp16 (11-bit significand; the sum l stays
+//   fp32). bf16: rounding P to bf16's 8 bits made ~0.1% of outputs miss half
+//   an output ulp against the exact result, so P is split into hi + lo bf16
+//   parts and V^T P^T takes two MFMAs per 16 dims.
+
+#include <type_traits>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+#include "pkv_mfma.h"
+
+namespace pkv {
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillQW = 2;                                        // 16-row tiles per wave
+constexpr int kPrefillRows = 16 * kPrefillQW * kPrefillWaves;        // rows per workgroup
+constexpr int kPrefillKeys = 64;                                     // keys per LDS stage
+constexpr int kVtRow = kPrefillKeys * 2 + 8;                         // bytes of one V^T row
+
+template <int D>
+constexpr int prefill_krow() { return 2 * D + 16; }
+
+int prefill_rows_per_tile() { return kPrefillRows; }
+
+template <typename T, int D, int BS>
+__global__ void __launch_bounds__(kPrefillWaves * 64)
+prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
+               const uint16_t* __restrict__ key_cache, const uint16_t* __restrict__ value_cache,
+               const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+               const int32_t* __restrict__ query_start, int num_heads, int max_blocks,
+               int q_tiles, float scale_log2) {
+  using E = Elem<T>;
+  using M = Mfma<T>;
+  constexpr int KROW = prefill_krow<D>();
+  constexpr int NK = D / 32;                      // S^T MFMAs per 16 keys
+  constexpr int NC = D / 16;                      // 16-dim output chunks
+  constexpr int QW = kPrefillQW;
+  constexpr int THREADS = kPrefillWaves * 64;
+  constexpr int PIECES = kPrefillKeys * D / 8;    // 16-byte pieces of K (or V) per stage
+  constexpr int PER_THREAD = PIECES / THREADS;
+  static_assert(PIECES % THREADS == 0, "whole pieces per thread");
+  __shared__ __align__(16) uint8_t s_k[kPrefillKeys * KROW];
+  __shared__ __align__(16) uint8_t s_vt[D * kVtRow];
+
+  const int H = num_heads;
+  const int h = blockIdx.x % H;
+  const int tile = q_tiles - 1 - (int)(blockIdx.x / H);
+  const int s = blockIdx.y;
+  const int q0 = query_start[s];
+  const int qn = query_start[s + 1] - q0;
+  if (tile * kPrefillRows >= qn) return;
+  const int ctx = context_lens[s];
+  const int first = ctx - qn;                     // position of chunk row 0
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int wrow0 = tile * kPrefillRows + wave * 16 * QW;   // this wave's first chunk row
+  const int wend = min(wrow0 + 16 * QW, qn);
+  const int wave_last_pos = first + wend - 1;               // meaningful when wrow0 < qn
+  const int nkeys = first + min(tile * kPrefillRows + kPrefillRows, qn);  // keys [0, nkeys)
+
+  uint4 qf[QW][NK];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    const int row = wrow0 + 16 * j + col;
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      qf[j][i] = row < qn ? *reinterpret_cast<const uint4*>(
+                                query + ((size_t)(q0 + row) * H + h) * D + 32 * i + 8 * grp)
+                          : make_uint4(0, 0, 0, 0);
+  }
+  f4_t acc[QW][NC];
+  float m[QW], l[QW];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[j][c] = f4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t kv_dim = (size_t)H * D;
+  const int32_t* bt = block_tables + (size_t)s * max_blocks;
+  // Piece it of this thread: key row r = q / (D/8) of the stage, 16-byte
+  // column cc = q % (D/8), q = threadIdx.x + it * THREADS. Keys past the
+  // last needed one re-read it (valid, a cache hit); the mask drops them.
+  uint4 pk[PER_THREAD], pv[PER_THREAD];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int it = 0; it < PER_THREAD; ++it) {
+      const int q = threadIdx.x + it * THREADS;
+      const int r = q / (D / 8);
+      const int cc = q % (D / 8);
+      const int kpos = min(st * kPrefillKeys + r, nkeys - 1);
+      const size_t slot = (size_t)bt[kpos / BS] * BS + (kpos % BS);
+      const size_t off = slot * kv_dim + (size_t)h * D + cc * 8;
+      pk[it] = *reinterpret_cast<const uint4*>(key_cache + off);
+      pv[it] = *reinterpret_cast<const uint4*>(value_cache + off);
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int it = 0; it < PER_THREAD; ++it) {
+      const int q = threadIdx.x + it * THREADS;
+      const int r = q / (D / 8);
+      const int cc = q % (D / 8);
+      *reinterpret_cast<uint4*>(s_k + r * KROW + cc * 16) = pk[it];
+      const uint32_t w[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * kVtRow + r * 2) =
+            (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  };
+
+  const int nstages = (nkeys + kPrefillKeys - 1) / kPrefillKeys;
+  load_stage(0);
+  for (int st = 0; st < nstages; ++st) {
+    __syncthreads();                  // every wave is done with the previous stage
+    store_stage();
+    __syncthreads();
+    if (st + 1 < nstages) load_stage(st + 1);
+    if (wrow0 >= qn) continue;        // a wave past the chunk's end only helps staging
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const int kbase = st * kPrefillKeys + kp * 32;     // first key of this 32-key step
+      if (kbase > wave_last_pos) break;                  // wave-uniform
+      const int lk = kp * 32;
+      uint4 ka[NK], kb[NK];
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        ka[i] = *reinterpret_cast<const uint4*>(s_k + (lk + col) * KROW + (32 * i + 8 * grp) * 2);
+        kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * KROW +
+                                                (32 * i + 8 * grp) * 2);
+      }
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        if (wrow0 + 16 * j >= qn) continue;              // wave-uniform
+        const int qpos = first + wrow0 + 16 * j + col;   // this lane's query position
+        f4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          sa = M::k32(ka[i], qf[j][i], sa);
+          sb = M::k32(kb[i], qf[j][i], sb);
+        }
+        float x[8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[v] = (kbase + 4 * grp + v <= qpos) ? sa[v] * scale_log2 : -INFINITY;
+          x[4 + v] = (kbase + 16 + 4 * grp + v <= qpos) ? sb[v] * scale_log2 : -INFINITY;
+        }
+        float bm = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, x[e]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        // The first step holds key 0, which every query sees, so m is finite
+        // from then on; a later step whose keys are all masked for a query
+        // leaves it unchanged (alpha = 1, p = 0).
+        const float mn = fmaxf(m[j], bm);
+        const float alpha = fast_exp2(m[j] - mn);
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(x[e] - mn);
+          ps += p[e];
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l[j] = l[j] * alpha + ps;
+        m[j] = mn;
+        constexpr bool kSplit = std::is_same<T, BF16>::value;
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = E::round(p[e]);
+          lo[e] = kSplit ? E::round(p[e] - M::widen(hi[e])) : 0u;
+        }
+        const uint4 bhi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                     hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+        const uint4 blo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                     lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint8_t* vrow = s_vt + (16 * c + col) * kVtRow;
+          const uint2 va = *reinterpret_cast<const uint2*>(vrow + (lk + 4 * grp) * 2);
+          const uint2 vb = *reinterpret_cast<const uint2*>(vrow + (lk + 16 + 4 * grp) * 2);
+          const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
+          f4_t t = M::k32(a, bhi, acc[j][c] * alpha);
+          if constexpr (kSplit) t = M::k32(a, blo, t);
+          acc[j][c] = t;
+        }
+      }
+    }
+  }
+
+  // acc[j][c][v] = O^T[dim 16c + 4g + v][row wrow0 + 16j + l%16], unnormalised
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    const int row = wrow0 + 16 * j + col;
+    if (row >= qn) continue;
+    const float inv = 1.f / l[j];
+    uint16_t* o = out + ((size_t)(q0 + row) * H + h) * D + 4 * grp;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t r0 = E::round(acc[j][c][0] * inv), r1 = E::round(acc[j][c][1] * inv);
+      const uint32_t r2 = E::round(acc[j][c][2] * inv), r3 = E::round(acc[j][c][3] * inv);
+      *reinterpret_cast<uint2*>(o + 16 * c) = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+    }
+  }
+}
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D, int BS>
+hipError_t prefill_t(const PrefillArgs& a, hipStream_t st) {
+  const int q_tiles = (a.max_query_len + kPrefillRows - 1) / kPrefillRows;
+  const dim3 grid((unsigned)(a.num_heads * q_tiles), (unsigned)a.num_seqs);
+  hipLaunchKernelGGL((prefill_kernel<T, D, BS>), grid, dim3(kPrefillWaves * 64), 0, st,
+                     static_cast<uint16_t*>(a.out), static_cast<const uint16_t*>(a.query),
+                     static_cast<const uint16_t*>(a.key_cache),
+                     static_cast<const uint16_t*>(a.value_cache), a.block_tables, a.context_lens,
+                     a.query_start, a.num_heads, a.max_blocks_per_seq, q_tiles,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t prefill_d(const PrefillArgs& a, hipStream_t st) {
+  if (a.block_size == 8) return prefill_t<T, D, 8>(a, st);
+  if (a.block_size == 32) return prefill_t<T, D, 32>(a, st);
+  return prefill_t<T, D, 16>(a, st);
+}
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  if (a.dtype == 0) return a.head_dim == 64 ? prefill_d<F16, 64>(a, st) : prefill_d<F16, 128>(a, st);
+  return a.head_dim == 64 ? prefill_d<BF16, 64>(a, st) : prefill_d<BF16, 128>(a, st);
+}
+
+}  // namespace pkv

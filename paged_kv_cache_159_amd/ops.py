@@ -146,6 +146,40 @@ def paged_attention_decode_grouped(out, query, key_cache, value_cache, block_tab
     return out
 
 
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
+                            query_start, scale: float, max_query_len: int | None = None,
+                            block_size: int | None = None) -> torch.Tensor:
+    """Causal attention of each sequence's chunk of new tokens (packed rows
+    query_start[s] .. query_start[s+1] of query and out, [T, H, D]) over its
+    paged context; the chunk's K/V must already be in the cache. Returns out.
+    ``max_query_len`` bounds every chunk; if omitted it is read from
+    query_start (one device-to-host copy)."""
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, query_start)
+    dt = _dtype_code(out, query, key_cache, value_cache)
+    _expect(block_tables, torch.int32, 2, "block_tables")
+    _expect(context_lens, torch.int32, 1, "context_lens")
+    _expect(query_start, torch.int32, 1, "query_start")
+    if query.dim() != 3 or key_cache.dim() != 4 or value_cache.shape != key_cache.shape:
+        raise ValueError("query [T,H,D] and caches [NB,bs,H,D] expected")
+    T, H, D = query.shape
+    NB, bs, H2, D2 = key_cache.shape
+    _block_size(key_cache, block_size)
+    if out.shape != query.shape or (H2, D2) != (H, D):
+        raise ValueError("out/query/cache shapes disagree")
+    S = context_lens.shape[0]
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("block_tables needs S rows and query_start S + 1 entries")
+    if max_query_len is None:
+        max_query_len = int(torch.diff(query_start).max().item()) if S else 0
+    rc = lib().paged_attention_prefill(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                                       value_cache.data_ptr(), block_tables.data_ptr(),
+                                       context_lens.data_ptr(), query_start.data_ptr(), S,
+                                       int(max_query_len), H, D, NB, bs, block_tables.shape[1],
+                                       float(scale), dt, _stream(out))
+    check("paged_attention_prefill", rc)
+    return out
+
+
 def paged_attention_decode_partitions(out, query, key_cache, value_cache, block_tables,
                                       context_lens, scale: float, workspace,
                                       block_size: int | None = None) -> None:

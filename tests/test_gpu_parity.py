@@ -589,3 +589,65 @@ def test_beam_search_llama_shape():
     from workloads import BeamSearch
     b = BeamSearch(prompts=16, beams=8, steps=3, dtype="bf16", seed=5, groups="prompt")
     _run_beam(b, 3)
+
+
+# ------------------------------------------------------------ prefill / chunked prefill
+
+def check_prefill(w, heads=None, format_bound=None, check_caches=True):
+    """reshape_and_cache of the chunks, then paged_attention_prefill; caches
+    bit-exact, attention against the oracle on the computed (row, head)s."""
+    pkv = _pkv()
+    say(f"prefill {w.name}: bs={w.block_size} S={w.num_seqs} H={w.num_heads} D={w.head_dim} "
+        f"{w.dtype} rows={w.query.shape[0]} ctx={w.context_lens.tolist()[:8]} heads={heads}")
+    dw = upload(w)
+    pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
+    pkv.paged_attention_prefill(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                dw.context_lens, dw.query_start, w.scale)
+    torch.cuda.synchronize()
+    K, V = oracle.reshape_and_cache(w.new_key, w.new_value, w.key_cache, w.value_cache,
+                                    w.slot_mapping, w.block_size)
+    if check_caches:
+        assert np.array_equal(device_to_bits(dw.key_cache), K), "key cache differs"
+        assert np.array_equal(device_to_bits(dw.value_cache), V), "value cache differs"
+    want = oracle.paged_attention_prefill(w.query, K, V, w.block_tables, w.context_lens,
+                                          w.query_start, w.scale, w.block_size, w.dtype,
+                                          heads=heads)
+    got = device_to_float64(dw.out)
+    sel = ~np.isnan(want)
+    assert_attention_close(got[sel], want[sel], what=f"prefill {w.name}", format_bound=format_bound)
+    return got, sel
+
+
+PREFILL_CHUNKS = [1, 16, 17, 100, 129, 300, 0, 5, 64]
+PREFILL_CACHED = [0, 0, 40, 0, 200, 33, 10, 1, 700]
+
+
+@pytest.mark.parametrize("bs", [16, 8, 32])
+@pytest.mark.parametrize("dtype,head_dim", [("f16", 128), ("bf16", 128), ("f16", 64), ("bf16", 64)])
+def test_prefill_chunks_and_prompts(dtype, head_dim, bs):
+    """Whole prompts (no cached tokens), chunks after a cached prefix, a
+    one-token chunk, an empty chunk, tiles of 128 rows with a ragged tail,
+    3 heads."""
+    from workloads import make_prefill_case
+    w = make_prefill_case(PREFILL_CHUNKS, PREFILL_CACHED, 3, head_dim, dtype,
+                          seed=head_dim + bs + (dtype == "bf16"), block_size=bs)
+    check_prefill(w, format_bound="bf16" if dtype == "bf16" else None)
+
+
+def test_prefill_canaries_not_read():
+    from workloads import make_prefill_case
+    w = make_prefill_case(PREFILL_CHUNKS, PREFILL_CACHED, 2, 128, "f16", seed=3)
+    clean, _ = check_prefill(w)
+    poisoned, _ = check_prefill(poison_unused(w), check_caches=False)
+    assert np.array_equal(clean, poisoned)
+
+
+@pytest.mark.parametrize("chunks,cached", [([2048, 1000, 512, 77], [0, 0, 0, 0]),
+                                           ([512, 700, 256, 64], [1536, 0, 256, 3000])])
+def test_prefill_llama_shape(chunks, cached):
+    """LLaMA-7B shape (32 heads x 128, fp16): whole prompts up to 2048 tokens
+    and chunks after cached prefixes up to 3064 tokens; the oracle checks 3
+    heads of every row, caches in full."""
+    from workloads import make_prefill_case
+    w = make_prefill_case(chunks, cached, 32, 128, "f16", seed=sum(chunks), name="prefill_llama")
+    check_prefill(w, heads=[0, 13, 31])

@@ -8,6 +8,6 @@ arithmetic lives here.
 from .allocator import BlockAllocator, SwapSpace  # noqa: F401
 from .beam import BeamSearch, BeamStep  # noqa: F401
 from .configs import (  # noqa: F401
-    BLOCK_SIZE, CONFIG_NAMES, Workload, make_config, make_decode_case, make_shared_case,
-    poison_unused,
+    BLOCK_SIZE, CONFIG_NAMES, Workload, make_config, make_decode_case, make_prefill_case,
+    make_shared_case, poison_unused,
 )

@@ -73,6 +73,7 @@ class Workload:
     copy_pairs: np.ndarray          # int32 [P, 2] (src, dst)
     group_start: np.ndarray | None = None   # int32 [G+1] sequence ranges sharing a prefix
     shared_blocks: np.ndarray | None = None  # int32 [G] leading blocks identical in a group
+    query_start: np.ndarray | None = None    # prefill only: int32 [S+1] rows of each chunk
     allocator: BlockAllocator | None = field(default=None, repr=False)
 
     @property
@@ -259,6 +260,42 @@ def make_shared_case(prompts, samples, prefix, suffix_lo, suffix_hi, num_heads, 
     st = np.random.SeedSequence(seed).spawn(8)
     return _shared_prefix(st, 0, "custom_shared", prompts, samples, prefix, suffix_lo, suffix_hi,
                           num_heads, head_dim, dtype, block_size)
+
+
+def make_prefill_case(chunk_lens, cached_lens, num_heads: int, head_dim: int, dtype: str = "f16",
+                      seed: int = 0, block_size: int = BLOCK_SIZE, max_blocks: int | None = None,
+                      name: str = "prefill") -> Workload:
+    """A prefill / chunked-prefill step: sequence s holds cached_lens[s] tokens
+    and the step appends a chunk of chunk_lens[s] tokens (pages taken as
+    needed, [P1] §3.3.2), writes their K/V with reshape_and_cache and attends
+    from each of them causally. ``query`` and the new K/V are packed [T, H, D]
+    with T = sum(chunk_lens); ``query_start`` gives each sequence's rows."""
+    chunk_lens = [int(c) for c in chunk_lens]
+    cached_lens = [int(c) for c in cached_lens]
+    if len(chunk_lens) != len(cached_lens) or min(chunk_lens) < 0 or min(cached_lens) < 0:
+        raise ValueError("one non-negative chunk and cached length per sequence")
+    st = np.random.SeedSequence(seed).spawn(8)
+    bs = block_size
+    ctx = [a + b for a, b in zip(chunk_lens, cached_lens)]
+    if min(ctx) < 1:
+        raise ValueError("every sequence needs at least one token")
+    needed = sum(_blocks(c, bs) for c in ctx)
+    pool = math.ceil(1.1 * needed) + 2
+    order = np.random.Generator(np.random.PCG64(st[1])).permutation(pool)
+    alloc = BlockAllocator(pool, bs, free_order=order)
+    seqs = list(range(len(ctx)))
+    for s in seqs:
+        alloc.allocate(s, cached_lens[s])
+    slots = []
+    for s in seqs:
+        alloc.append_tokens(s, chunk_lens[s])
+        slots += [alloc.slot(s, p) for p in range(cached_lens[s], ctx[s])]
+    mb = max_blocks if max_blocks is not None else max(_blocks(c, bs) for c in ctx)
+    w = _finish(0, name, dtype, num_heads, head_dim, alloc, seqs, ctx, mb, st, len(slots), slots, [])
+    T = len(slots)
+    w.query = _normal_bits(st[7], T * num_heads * head_dim, dtype).reshape(T, num_heads, head_dim)
+    w.query_start = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int32)
+    return w
 
 
 def poison_unused(w: Workload) -> Workload:

@@ -40,6 +40,7 @@ class DeviceWorkload:
     slot_mapping: torch.Tensor
     copy_pairs: torch.Tensor
     out: torch.Tensor
+    query_start: torch.Tensor | None = None
 
 
 def upload(w: Workload, device="cuda") -> DeviceWorkload:
@@ -55,4 +56,6 @@ def upload(w: Workload, device="cuda") -> DeviceWorkload:
         slot_mapping=torch.from_numpy(np.ascontiguousarray(w.slot_mapping)).to(device),
         copy_pairs=torch.from_numpy(np.ascontiguousarray(w.copy_pairs)).to(device),
         out=torch.empty_like(q),
+        query_start=None if w.query_start is None
+        else torch.from_numpy(np.ascontiguousarray(w.query_start)).to(device),
     )
