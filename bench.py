@@ -71,6 +71,12 @@ def parse():
                     help="measure beam-search decoding instead: 16 prompts x 8 beams at the "
                          "LLaMA-7B shape, 32 steps of CoW copy + cache write + decode (grouped "
                          "by prompt, grouped by parent, and plain); prints its own JSON line")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure paged_attention_prefill instead: whole prompts (8 x "
+                         "1024..4096 tokens) and chunks (16 x 512 after 1024..3072 cached), "
+                         "LLaMA-7B shape; prints its own JSON line")
+    ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
+                    help="element type of the --prefill workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -401,6 +407,73 @@ def beam_bench(args, dev):
     print(json.dumps(res), flush=True)
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16 / bf16
+
+
+def prefill_flops(w):
+    """Algorithmic flops of the causal prefill: per head, each query at
+    position p takes p + 1 keys, 2*D flops each for q.k and for p.v."""
+    qs, ctx = w.query_start.astype(np.int64), w.context_lens.astype(np.int64)
+    n = np.diff(qs)
+    first = ctx - n
+    keys = n * first + n * (n + 1) // 2
+    return int(4 * w.head_dim * w.num_heads * keys.sum())
+
+
+def prefill_bench(args, dev):
+    import torch
+
+    import paged_kv_cache_159_amd as pkv
+    from workloads import make_prefill_case
+    from workloads.device import upload
+
+    rng = np.random.default_rng(2024)
+    cases = {
+        "whole_prompts": ([int(x) for x in rng.integers(1024, 4096, size=8, endpoint=True)],
+                          [0] * 8),
+        "chunks_512": ([512] * 16, [int(x) for x in rng.integers(1024, 3072, size=16, endpoint=True)]),
+    }
+    res = {"metric": "paged prefill attention TFLOP/s (MFMA)", "unit": "TFLOP/s",
+           "data": "synthetic", "dtype": args.dtype}
+    for name, (chunks, cached) in cases.items():
+        w = make_prefill_case(chunks, cached, 32, 128, args.dtype, seed=len(name),
+                              block_size=args.block_size, name=name)
+        dw = upload(w, dev)
+        pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
+        mq = max(chunks)
+        f = lambda: pkv.paged_attention_prefill(dw.out, dw.query, dw.key_cache, dw.value_cache,
+                                                dw.block_tables, dw.context_lens, dw.query_start,
+                                                w.scale, max_query_len=mq)
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(max(5, min(args.steps, 30))):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        fl = prefill_flops(w)
+        tf = fl / (us * 1e-6) / 1e12
+        res[name] = {"kernel_us": round(us, 1), "flops": fl, "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS[args.dtype], 4),
+                     "tokens": int(sum(chunks)), "tokens_per_s": round(sum(chunks) / (us * 1e-6), 1),
+                     "chunks": chunks, "cached": cached}
+        del dw
+        torch.cuda.empty_cache()
+    res["value"] = res["whole_prompts"]["tflops"]
+    res["roofline"] = {"bound": "mfma", "achieved": res["whole_prompts"]["tflops"],
+                       "peak": MFMA_PEAK_TFLOPS[args.dtype], "unit": "TFLOP/s",
+                       "frac": res["whole_prompts"]["frac_of_peak"],
+                       "kernel": "prefill_kernel"}
+    res["config"] = {"workload": f"prefill, 32 heads x 128, {args.dtype}, block_size {args.block_size}"}
+    print(json.dumps(res), flush=True)
+
+
 def load_traffic(key):
     """HBM traffic per decode launch from committed rocprofv3 counter runs,
     only if they were taken on the current decode kernel source."""
@@ -461,10 +534,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.beam:
+    if args.beam or args.prefill:
         import torch
         torch.cuda.set_device(0)
-        beam_bench(args, torch.device("cuda", 0))
+        (beam_bench if args.beam else prefill_bench)(args, torch.device("cuda", 0))
         return
     if args.traffic_summary:
         sys.path.insert(0, ROOT)
