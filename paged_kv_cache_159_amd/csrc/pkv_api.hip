@@ -97,6 +97,7 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->num_groups = 0;
   a->ws_ml = nullptr;
   a->ws_o = nullptr;
+  a->ws_seq = nullptr;
   if (need) pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a->ws_ml, &a->ws_o);
   return PKV_OK;
 }
@@ -121,7 +122,9 @@ int check_grouped(int num_seqs, int num_heads, int head_dim, int block_size,
   if ((int64_t)num_groups * (*chunk_slots) * num_heads + (int64_t)num_seqs * num_heads * slots >
       kMaxGrid)
     return PKV_ERR_SHAPE;
-  *need = pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)slots);
+  // partials, then one int32 per sequence (its shared-prefix token count)
+  *need = pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, (int)slots) +
+          (size_t)num_seqs * sizeof(int32_t);
   return PKV_OK;
 }
 
@@ -310,6 +313,9 @@ int paged_attention_decode_grouped(void* out, const void* query, const void* key
   a.scale = scale;
   a.dtype = dtype;
   pkv::decode_workspace_split(workspace, num_seqs, num_heads, a.num_parts, &a.ws_ml, &a.ws_o);
+  a.ws_seq = reinterpret_cast<int32_t*>(
+      static_cast<char*>(workspace) +
+      pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, a.num_parts));
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = status_of(pkv::launch_decode_grouped(a, st));
   if (rc) return rc;

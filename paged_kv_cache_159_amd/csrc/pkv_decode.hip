@@ -58,12 +58,12 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         int max_blocks, int num_parts, float scale_log2,
                         const int32_t* __restrict__ group_start,
                         const int32_t* __restrict__ shared_blocks, int num_groups,
-                        int slot_base) {
+                        int slot_base, int32_t* __restrict__ seq_tok0) {
   __shared__ __align__(16) uint8_t lds[partition_lds_bytes<D>()];
   partition_body<T, D, PT, BS, TAIL>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
-                                 block_tables, context_lens, num_seqs, num_heads, max_blocks,
-                                 num_parts, scale_log2, group_start, shared_blocks, num_groups,
-                                 slot_base, lds);
+                                     block_tables, context_lens, num_seqs, num_heads, max_blocks,
+                                     num_parts, scale_log2, group_start, shared_blocks,
+                                     num_groups, slot_base, seq_tok0, lds);
 }
 
 // Log-sum-exp merge of the partials of one (sequence, head). Partials live in
@@ -80,9 +80,7 @@ __global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
                     const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens,
                     int num_heads, int num_parts, int part_tokens,
-                    const int32_t* __restrict__ group_start,
-                    const int32_t* __restrict__ shared_blocks, int num_groups, int block_size,
-                    int slot_base) {
+                    const int32_t* __restrict__ seq_tok0, int slot_base) {
   using E = Elem<T>;
   constexpr int K = kMergeThreads / D;
   const int H = num_heads;
@@ -92,8 +90,7 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
   int n0, n1;
   if constexpr (GROUPED) {
     constexpr int chunk_tokens = kSharedChunkTiles * kTileTokens;
-    const int st = shared_prefix_tokens(shared_blocks[group_of(s, group_start, num_groups)],
-                                        block_size);
+    const int st = seq_tok0[s];   // shared-prefix tokens, written by the main launch
     n0 = (st + chunk_tokens - 1) / chunk_tokens;
     n1 = (ctx - st + part_tokens - 1) / part_tokens;
   } else {
@@ -168,7 +165,8 @@ hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
                      static_cast<const uint16_t*>(a.key_cache),
                      static_cast<const uint16_t*>(a.value_cache), a.block_tables, a.context_lens,
                      a.num_seqs, a.num_heads, a.max_blocks_per_seq, a.num_parts,
-                     a.scale * kLog2e, a.group_start, a.shared_blocks, a.num_groups, a.slot_base);
+                     a.scale * kLog2e, a.group_start, a.shared_blocks, a.num_groups, a.slot_base,
+                     a.ws_seq);
   return hipGetLastError();
 }
 
@@ -192,16 +190,14 @@ hipError_t partitions_d(const DecodeArgs& a, hipStream_t st) {
 template <typename T, int D>
 hipError_t merge_t(const DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.num_seqs * a.num_heads;
-  if (a.group_start != nullptr) {
+  if (a.ws_seq != nullptr) {
     hipLaunchKernelGGL((decode_merge_kernel<T, D, true>), dim3(grid), dim3(kMergeThreads), 0, st,
                        static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
-                       a.num_parts, a.part_tokens, a.group_start, a.shared_blocks, a.num_groups,
-                       a.block_size, a.slot_base);
+                       a.num_parts, a.part_tokens, a.ws_seq, a.slot_base);
   } else {
     hipLaunchKernelGGL((decode_merge_kernel<T, D, false>), dim3(grid), dim3(kMergeThreads), 0, st,
                        static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens, a.num_heads,
-                       a.num_parts, a.part_tokens, a.group_start, a.shared_blocks, a.num_groups,
-                       a.block_size, 0);
+                       a.num_parts, a.part_tokens, nullptr, 0);
   }
   return hipGetLastError();
 }

@@ -196,7 +196,7 @@ __device__ __forceinline__ void shared_unit(
 // they overlap on the machine; the tails (several blocks per sequence and head
 // group) are dispatched first and the short shared units fill in behind them.
 template <typename T, int D, int PT, int BS>
-__global__ void __launch_bounds__(kGroupedWaves * 64)
+__global__ void __launch_bounds__(kGroupedWaves * 64, 8)
 decode_grouped_kernel(float* __restrict__ ws_ml, float* __restrict__ ws_o,
                       const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
                       const uint16_t* __restrict__ value_cache,
@@ -205,7 +205,7 @@ decode_grouped_kernel(float* __restrict__ ws_ml, float* __restrict__ ws_o,
                       const int32_t* __restrict__ group_start,
                       const int32_t* __restrict__ shared_blocks, int num_groups, int num_seqs,
                       int num_heads, int max_blocks, int num_parts, int chunk_slots,
-                      int tail_wgs, float scale_log2) {
+                      int tail_wgs, float scale_log2, int32_t* __restrict__ seq_tok0) {
   constexpr int kLds = shared_lds_bytes<D>() > partition_lds_bytes<D>() ? shared_lds_bytes<D>()
                                                                          : partition_lds_bytes<D>();
   __shared__ __align__(16) uint8_t lds[kLds];
@@ -213,7 +213,7 @@ decode_grouped_kernel(float* __restrict__ ws_ml, float* __restrict__ ws_o,
     partition_body<T, D, PT, BS, true>(blockIdx.x, nullptr, ws_ml, ws_o, query, key_cache,
                                    value_cache, block_tables, context_lens, num_seqs, num_heads,
                                    max_blocks, num_parts, scale_log2, group_start, shared_blocks,
-                                   num_groups, chunk_slots, lds);
+                                   num_groups, chunk_slots, seq_tok0, lds);
   } else {
     const int u = blockIdx.x - tail_wgs;
     const int h = u % num_heads;
@@ -241,7 +241,7 @@ hipError_t grouped_t(const DecodeArgs& a, hipStream_t st) {
                      static_cast<const uint16_t*>(a.value_cache), a.block_tables, a.context_lens,
                      a.group_start, a.shared_blocks, a.num_groups, a.num_seqs, a.num_heads,
                      a.max_blocks_per_seq, a.num_parts, chunk_slots, (int)tail_wgs,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, a.ws_seq);
   return hipGetLastError();
 }
 

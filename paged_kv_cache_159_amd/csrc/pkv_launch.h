@@ -38,6 +38,8 @@ struct DecodeArgs {
   int dtype;            // 0 fp16, 1 bf16
   float* ws_ml;         // [num_seqs][num_heads][num_parts][2] (running max, exp sum), log2 domain
   float* ws_o;          // [num_seqs][num_heads][num_parts][head_dim] normalised partial outputs
+  int32_t* ws_seq;      // grouped call: [num_seqs] shared-prefix tokens of each sequence,
+                        // written by the main launch, read by the merge
 };
 
 // Tokens per context partition for these sizes (256 or 512).

@@ -7,6 +7,12 @@
 namespace pkv {
 
 constexpr int kWaves = 8;
+#ifndef PKV_TILES_PER_STEP
+#define PKV_TILES_PER_STEP 1
+#endif
+// 16-token tiles each loop step covers: every wave has 2 * kTilesPerStep rows
+// of K and V in flight per step.
+constexpr int kTilesPerStep = PKV_TILES_PER_STEP;
 
 // LDS bytes partition_body needs: per wave and head (max, sum), and per wave a
 // head group's accumulators.
@@ -23,8 +29,9 @@ constexpr int partition_lds_bytes() {
 // and w + 8 of every tile, each through the block table. TAIL = true is the
 // grouped call's tail:
 // each sequence starts after its group's shared-prefix tiles (handled by the
-// shared-prefix units), its partitions go to partial slots slot_base + p, and
-// every partition writes a partial (the merge always runs).
+// shared-prefix units), its partitions go to partial slots slot_base + p,
+// every partition writes a partial (the merge always runs), and the sequence's
+// shared-prefix token count goes to seq_tok0[s] for the merge.
 template <typename T, int D, int PT, int BS, bool TAIL>
 __device__ __forceinline__ void partition_body(
     int wg, uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
@@ -32,13 +39,15 @@ __device__ __forceinline__ void partition_body(
     const uint16_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int num_seqs, int num_heads, int max_blocks,
     int num_parts, float scale_log2, const int32_t* __restrict__ group_start,
-    const int32_t* __restrict__ shared_blocks, int num_groups, int slot_base, uint8_t* lds) {
+    const int32_t* __restrict__ shared_blocks, int num_groups, int slot_base,
+    int32_t* __restrict__ seq_tok0, uint8_t* lds) {
   using E = Elem<T>;
   constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
   constexpr int HG = 64 / LPR;       // heads per wave-wide load
-  constexpr int RPW = kTileTokens / kWaves;  // rows of a tile each wave reads
-  static_assert(PT % BS == 0 && PT % kTileTokens == 0, "partition is whole blocks and tiles");
-  static_assert(BS % 8 == 0 && RPW == 2, "tile rows w and w + 8 are in blocks of >= 8 tokens");
+  constexpr int STEP = kTileTokens * kTilesPerStep;    // tokens per loop step
+  constexpr int RPW = STEP / kWaves;                  // rows each wave reads per step
+  static_assert(PT % BS == 0 && PT % STEP == 0, "partition is whole blocks and steps");
+  static_assert(BS % 8 == 0, "rows w, w + 8, ... of a step lie in blocks of >= 8 tokens");
   static_assert(PT / BS <= 64, "a partition's table entries fit one per lane");
 
   const int H = num_heads;
@@ -51,11 +60,14 @@ __device__ __forceinline__ void partition_body(
   int tok0 = 0;   // first token this launch covers for sequence s
   if constexpr (TAIL)
     tok0 = shared_prefix_tokens(shared_blocks[group_of(s, group_start, num_groups)], BS);
+  if constexpr (TAIL) {
+    if (p == 0 && g == 0 && threadIdx.x == 0) seq_tok0[s] = tok0;
+  }
   const int tok_begin = tok0 + p * PT;
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + PT);
   // tok0 (a multiple of 16) and PT are multiples of the tile and the block
-  const int ntiles = (tok_end - tok_begin + kTileTokens - 1) / kTileTokens;
+  const int nsteps = (tok_end - tok_begin + STEP - 1) / STEP;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -84,10 +96,10 @@ __device__ __forceinline__ void partition_body(
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
-  for (int k = 0; k < ntiles; ++k) {
-    const int tb = tok_begin + k * kTileTokens;   // < ctx
+  for (int k = 0; k < nsteps; ++k) {
+    const int tb = tok_begin + k * STEP;   // < ctx
     // Token tb + wave + 8i, wave-uniform. Tokens past the context re-read the
-    // tile's first token (valid, a cache hit) instead of branching; their
+    // step's first token (valid, a cache hit) instead of branching; their
     // weight is exactly 0 below. Address: the block's base (64-bit, scalar)
     // plus the row and the lane's column (32-bit).
     uint4 kr[RPW], vr[RPW];
@@ -95,8 +107,10 @@ __device__ __forceinline__ void partition_body(
     for (int i = 0; i < RPW; ++i) {
       const uint32_t t = (uint32_t)(tb + wave + i * kWaves);
       const uint32_t te = t < (uint32_t)ctx ? t : (uint32_t)tb;
-      // At block sizes >= 16 the whole tile sits in the block of tb.
-      const uint32_t bi = (BS >= kTileTokens ? (uint32_t)tb : te) / BS - blk0;
+      // With one tile per step at block sizes >= 16, the tile sits in the
+      // block of tb.
+      const uint32_t bi =
+          ((kTilesPerStep == 1 && BS >= kTileTokens) ? (uint32_t)tb : te) / BS - blk0;
       const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(table_lane, bi);
       const uint32_t off = (te % BS) * row_bytes + col_bytes;
       kr[i] = *reinterpret_cast<const uint4*>(kpool + (size_t)phys * blk_bytes + off);

@@ -131,7 +131,7 @@ def _expected_grouped_workspace(S, H, D, MB, bs=16):
     tokens = MB * bs
     pt = 256 if tokens <= 4096 else 512
     n = S * H * (-(-tokens // 128) + -(-tokens // pt))
-    return ((n * 8 + 255) // 256) * 256 + n * D * 4
+    return ((n * 8 + 255) // 256) * 256 + n * D * 4 + 4 * S
 
 
 def test_grouped_workspace_size(L):
