@@ -12,7 +12,7 @@
 // attends over tokens 0 .. ctx - q_len + i through the block table. q_len = ctx
 // is a whole prompt, q_len < ctx a chunk after a cached prefix.
 //
-// Work decomposition. One 4-wave workgroup per (sequence, tile of 128 chunk
+// Work decomposition. One 8-wave workgroup per (sequence, tile of 256 chunk
 // rows, head); each wave owns 32 query rows as two 16-column MFMA tiles. Tiles
 // are dispatched last-first (the causal work of a tile grows with its
 // position). Keys are staged through LDS 64 at a time, gathered row by row
@@ -44,11 +44,27 @@
 
 namespace pkv {
 
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillQW = 2;                                        // 16-row tiles per wave
+// Shape measured on MI355X (LLaMA-7B heads, 8 prompts of 1.3k-3.8k tokens):
+// 8 waves x 2 query tiles x 64-key stages ~400 TFLOP/s fp16; 4 waves x 2
+// tiles (one wave per SIMD at 274 registers) 222; 8 x 1 373; 128-key stages
+// 330; the table copied to LDS, or V^T operands read once for both query
+// tiles, no gain.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+#ifndef PKV_PREFILL_QW
+#define PKV_PREFILL_QW 2
+#endif
+#ifndef PKV_PREFILL_KEYS
+#define PKV_PREFILL_KEYS 64
+#endif
+constexpr int kPrefillWaves = PKV_PREFILL_WAVES;
+constexpr int kPrefillQW = PKV_PREFILL_QW;                           // 16-row tiles per wave
 constexpr int kPrefillRows = 16 * kPrefillQW * kPrefillWaves;        // rows per workgroup
-constexpr int kPrefillKeys = 64;                                     // keys per LDS stage
-constexpr int kVtRow = kPrefillKeys * 2 + 8;                         // bytes of one V^T row
+constexpr int kPrefillKeys = PKV_PREFILL_KEYS;                       // keys per LDS stage
+// Bytes of one V^T row: the keys plus padding that keeps the 8-byte operand
+// reads of 32 lanes (16 dims x 2 key groups) on distinct LDS banks.
+constexpr int kVtRow = kPrefillKeys * 2 + (kPrefillKeys == 64 ? 8 : 16);
 
 template <int D>
 constexpr int prefill_krow() { return 2 * D + 16; }
@@ -156,7 +172,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     if (st + 1 < nstages) load_stage(st + 1);
     if (wrow0 >= qn) continue;        // a wave past the chunk's end only helps staging
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
+    for (int kp = 0; kp < kPrefillKeys / 32; ++kp) {
       const int kbase = st * kPrefillKeys + kp * 32;     // first key of this 32-key step
       if (kbase > wave_last_pos) break;                  // wave-uniform
       const int lk = kp * 32;

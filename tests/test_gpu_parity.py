@@ -626,7 +626,7 @@ PREFILL_CACHED = [0, 0, 40, 0, 200, 33, 10, 1, 700]
 @pytest.mark.parametrize("dtype,head_dim", [("f16", 128), ("bf16", 128), ("f16", 64), ("bf16", 64)])
 def test_prefill_chunks_and_prompts(dtype, head_dim, bs):
     """Whole prompts (no cached tokens), chunks after a cached prefix, a
-    one-token chunk, an empty chunk, tiles of 128 rows with a ragged tail,
+    one-token chunk, an empty chunk, 256-row tiles with a ragged tail (300 rows),
     3 heads."""
     from workloads import make_prefill_case
     w = make_prefill_case(PREFILL_CHUNKS, PREFILL_CACHED, 3, head_dim, dtype,
