@@ -65,6 +65,17 @@ constexpr int kPrefillKeys = PKV_PREFILL_KEYS;                       // keys per
 // Bytes of one V^T row: the keys plus padding that keeps the 8-byte operand
 // reads of 32 lanes (16 dims x 2 key groups) on distinct LDS banks.
 constexpr int kVtRow = kPrefillKeys * 2 + (kPrefillKeys == 64 ? 8 : 16);
+#ifndef PKV_VT_SWIZZLE
+#define PKV_VT_SWIZZLE 1
+#endif
+// Byte offset of key k in V^T row d: groups of 4 keys (one 8-byte MFMA
+// operand read) are XOR-swizzled by bits 5..6 of d, so the transposed 2-byte
+// stores of a wave (16 column pieces of 8 dims each, 4 keys) fall on distinct
+// LDS banks; the 16 lanes of an operand read share d >> 5, hence one swizzle.
+__device__ __forceinline__ int vt_key_offset(int d, int k) {
+  if (PKV_VT_SWIZZLE) return ((((k >> 2) ^ ((d >> 5) & 3)) << 2) | (k & 3)) * 2;
+  return k * 2;
+}
 
 template <int D>
 constexpr int prefill_krow() { return 2 * D + 16; }
@@ -158,7 +169,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       const uint32_t w[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * kVtRow + r * 2) =
+        *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * kVtRow + vt_key_offset(cc * 8 + e, r)) =
             (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   };
@@ -232,9 +243,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
                                      lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const uint8_t* vrow = s_vt + (16 * c + col) * kVtRow;
-          const uint2 va = *reinterpret_cast<const uint2*>(vrow + (lk + 4 * grp) * 2);
-          const uint2 vb = *reinterpret_cast<const uint2*>(vrow + (lk + 16 + 4 * grp) * 2);
+          const int d = 16 * c + col;
+          const uint8_t* vrow = s_vt + d * kVtRow;
+          const uint2 va = *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 4 * grp));
+          const uint2 vb =
+              *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 16 + 4 * grp));
           const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
           f4_t t = M::k32(a, bhi, acc[j][c] * alpha);
           if constexpr (kSplit) t = M::k32(a, blo, t);
