@@ -138,8 +138,7 @@ __device__ __forceinline__ void shared_unit(
 #pragma unroll
       for (int v = 0; v < 4; ++v) x[v] = sacc[v] * scale_log2;
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      bm = lane_group4_max(bm);
       const float mn = fmaxf(m, bm);
       const float alpha = fast_exp2(m - mn);
       float pr[4], ps = 0.f;
@@ -148,8 +147,7 @@ __device__ __forceinline__ void shared_unit(
         pr[v] = fast_exp2(x[v] - mn);
         ps += pr[v];
       }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = lane_group4_sum(ps);
       l = l * alpha + ps;
       m = mn;
       acc *= alpha;

@@ -49,4 +49,29 @@ template <> struct Mfma<BF16> {
   static __device__ __forceinline__ float widen(uint32_t x) { return __uint_as_float(x << 16); }
 };
 
+// Max / sum over the 4 lane groups of an MFMA tile (lanes l, l^16, l^32,
+// l^48: one column of the accumulator) with gfx950's row-swap instructions
+// instead of LDS permutes. With both operands equal to x, v_permlane16_swap
+// returns x's even 16-lane rows in both rows of each pair in one result and
+// its odd rows in the other (measured on the device), so combining the two
+// gives op(x[l], x[l^16]) in every lane; v_permlane32_swap does the same
+// across the two 32-lane halves. The two inputs of each combine are taken in
+// the same order in every lane, so all lanes get bit-identical results.
+__device__ __forceinline__ float lane_group4_max(float v) {
+  const unsigned x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned y = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_group4_sum(float v) {
+  const unsigned x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned y = __float_as_uint(s);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace pkv

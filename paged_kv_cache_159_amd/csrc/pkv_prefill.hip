@@ -26,7 +26,7 @@
 //   rows), two 16-key tiles; the accumulator holds S^T[key 4g+v][query l%16].
 //   Causal mask (key position > query position -> -inf), online softmax per
 //   query column in the log2 domain (max and sum across the 4 lane groups by
-//   two shuffles).
+//   gfx950's row-swap instructions).
 //   O^T += V^T P^T with one v_mfma_f32_16x16x32 per 16 output dims: its K index
 //   8g+e runs over keys 4g+e of the first tile (e < 4) and 16+4g+(e-4) of the
 //   second, which is exactly where the two S^T accumulators already hold P^T,
@@ -213,8 +213,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         float bm = x[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) bm = fmaxf(bm, x[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = lane_group4_max(bm);
         // The first step holds key 0, which every query sees, so m is finite
         // from then on; a later step whose keys are all masked for a query
         // leaves it unchanged (alpha = 1, p = 0).
@@ -226,8 +225,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           p[e] = fast_exp2(x[e] - mn);
           ps += p[e];
         }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
+        ps = lane_group4_sum(ps);
         l[j] = l[j] * alpha + ps;
         m[j] = mn;
         constexpr bool kSplit = std::is_same<T, BF16>::value;
