@@ -32,11 +32,14 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention KV GB/s + seqs/s, % of MI355X HBM peak (LLaMA-7B shape)"
+# Sources of the kernels a timed decode launch runs, per path; committed
+# counter traffic is used only while their digest matches.
 DECODE_SOURCES = ["paged_kv_cache_159_amd/csrc/pkv_decode.hip",
-                  "paged_kv_cache_159_amd/csrc/pkv_grouped.hip",
                   "paged_kv_cache_159_amd/csrc/pkv_partition.h",
                   "paged_kv_cache_159_amd/csrc/pkv_launch.h",
                   "paged_kv_cache_159_amd/csrc/pkv_device.h"]
+GROUPED_SOURCES = DECODE_SOURCES + ["paged_kv_cache_159_amd/csrc/pkv_grouped.hip",
+                                    "paged_kv_cache_159_amd/csrc/pkv_mfma.h"]
 # Kernels whose dispatches make up one timed decode launch, per mode.
 TIMED_KERNELS = {"plain": ("decode_partition_kernel",),
                  "grouped": ("decode_grouped_kernel", "decode_merge_kernel")}
@@ -129,9 +132,9 @@ def algorithmic_bytes(w):
     return decode, write, copy, logical
 
 
-def source_digest():
+def source_digest(grouped=False):
     h = hashlib.sha256()
-    for p in DECODE_SOURCES:
+    for p in (GROUPED_SOURCES if grouped else DECODE_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -193,7 +196,7 @@ def traffic_summary(paths, w, grouped):
         "workload": f"{w.name} ({w.num_seqs} seqs x {w.num_heads} heads x {w.head_dim}, {w.dtype}, "
                     f"bs {w.block_size}, sum ctx {w.total_context})",
         "mode": "grouped" if grouped else "plain",
-        "decode_source_digest": source_digest(),
+        "decode_source_digest": source_digest(grouped),
         "fetch_size_kib_per_dispatch": {n: round(v, 1) for n, v in fk.items()},
         "write_size_kib_per_dispatch": {n: round(v, 1) for n, v in wk.items()},
         "dispatches": nf,
@@ -482,7 +485,7 @@ def load_traffic(key):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("decode_source_digest") != source_digest():
+    if t.get("decode_source_digest") != source_digest(key.endswith("_grouped")):
         return None
     return t.get("bytes_per_launch")
 
