@@ -300,11 +300,20 @@ def swap_bench(args, w, dw, dev):
                                               method="dma"), n)
     t_in_dma = timed(lambda: pkv.swap_blocks(hk, hv, dw.key_cache, dw.value_cache, mi_h,
                                              method="dma"), n)
+    gbs = lambda t: nbytes / t / 1e9
+    staged = {}
+    for mib in (64, 256):
+        stg = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+        t_i = timed(lambda: pkv.swap_blocks(hk, hv, dw.key_cache, dw.value_cache, mi_h,
+                                            method="staged", staging=stg), n)
+        t_o = timed(lambda: pkv.swap_blocks(dw.key_cache, dw.value_cache, hk, hv, mo_h,
+                                            method="staged", staging=stg), n)
+        staged[f"{mib}MiB"] = {"swap_in_gbs": round(gbs(t_i), 2), "swap_out_gbs": round(gbs(t_o), 2)}
+        del stg
     runs_out = 1 + int(np.count_nonzero(np.any(np.diff(out_pairs, axis=0) != 1, axis=1)))
     runs_in = 1 + int(np.count_nonzero(np.any(np.diff(in_pairs, axis=0) != 1, axis=1)))
     t_d2h = timed(lambda: flat_host.copy_(flat_dev, non_blocking=True), n)
     t_h2d = timed(lambda: flat_dev.copy_(flat_host, non_blocking=True), n)
-    gbs = lambda t: nbytes / t / 1e9
     res = {
         "metric": "swap_blocks host-link GB/s (swap-out, swap-in)",
         "value": round(gbs(t_out), 2),
@@ -316,6 +325,7 @@ def swap_bench(args, w, dw, dev):
         "swap_in_ms": round(t_in * 1e3, 3),
         "dma": {"swap_out_gbs": round(gbs(t_out_dma), 2), "swap_in_gbs": round(gbs(t_in_dma), 2),
                 "copies_per_pool": {"out": runs_out, "in": runs_in}},
+        "staged": staged,
         "contiguous_pinned_copy_gbs": {"d2h": round(gbs(t_d2h), 2), "h2d": round(gbs(t_h2d), 2)},
         "roofline": {"bound": "host link", "peak": PCIE5_X16_GBS, "unit": "GB/s",
                      "frac_out": round(gbs(t_out) / PCIE5_X16_GBS, 4),

@@ -284,6 +284,30 @@ int swap_blocks_dma(const void* src_key, const void* src_value, void* dst_key, v
                     int src_num_blocks, int dst_num_blocks, int block_size, int dtype,
                     void* stream);
 
+/*
+ * Swap-in through a device staging buffer: the same block moves as
+ * swap_blocks / swap_blocks_dma (typically src = pinned host pools, dst =
+ * device pools), done as DMA of each run of consecutive source ids into
+ * consecutive staging slots (hipMemcpyAsync), then one block-copy launch that
+ * scatters the slots to their destination blocks. Swapped-out sequences sit
+ * in consecutive host blocks while their device blocks are scattered, so the
+ * DMA moves long runs instead of one block per copy. Pairs are processed in
+ * mapping order in chunks that fit `staging`, all on `stream`.
+ *   block_mapping  int32 [num_pairs][2], HOST memory, read during the call;
+ *                  every id is checked against its pool (PKV_ERR_SHAPE).
+ *   staging        device memory, 256-byte aligned: first the scatter mapping
+ *                  (num_pairs * 8 bytes, rounded up to 256), then a chunk of
+ *                  (staging_bytes - that) / (2 * block_bytes) K and V slots
+ *                  (block_bytes = block_size * num_heads * head_dim * 2); at
+ *                  least one slot, else PKV_ERR_WORKSPACE.
+ * Pools and staging as for swap_blocks (PKV_ERR_MEMORY otherwise).
+ */
+int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key,
+                       void* dst_value, const int32_t* block_mapping, int num_pairs,
+                       int num_heads, int head_dim, int src_num_blocks, int dst_num_blocks,
+                       int block_size, int dtype, void* staging, size_t staging_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,7 @@ EXPORTS = (
     "copy_blocks",
     "swap_blocks",
     "swap_blocks_dma",
+    "swap_blocks_staged",
 )
 
 PKV_F16, PKV_BF16 = 0, 1
@@ -58,6 +59,7 @@ _SIGNATURES = {
     "copy_blocks": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "swap_blocks": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
     "swap_blocks_dma": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
+    "swap_blocks_staged": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _z, _p]),
 }
 
 

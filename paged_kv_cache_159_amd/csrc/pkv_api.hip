@@ -6,6 +6,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "paged_kv.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -470,6 +473,80 @@ int swap_blocks_dma(const void* src_key, const void* src_value, void* dst_key, v
             hipSuccess)
       return PKV_ERR_LAUNCH;
     i += n;
+  }
+  return PKV_OK;
+}
+
+
+int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key,
+                       void* dst_value, const int32_t* block_mapping, int num_pairs,
+                       int num_heads, int head_dim, int src_num_blocks, int dst_num_blocks,
+                       int block_size, int dtype, void* staging, size_t staging_bytes,
+                       void* stream) {
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, src_num_blocks);
+  if (rc) return rc;
+  if (dst_num_blocks < 1 || num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_key || !src_value || !dst_key || !dst_value || !block_mapping || !staging)
+    return PKV_ERR_NULL;
+  if (!aligned16(src_key) || !aligned16(src_value) || !aligned16(dst_key) ||
+      !aligned16(dst_value) || !aligned4(block_mapping) ||
+      (reinterpret_cast<uintptr_t>(staging) & 255u))
+    return PKV_ERR_ALIGN;
+  for (int i = 0; i < num_pairs; ++i) {
+    const int32_t sb = block_mapping[2 * i], db = block_mapping[2 * i + 1];
+    if (sb < 0 || sb >= src_num_blocks || db < 0 || db >= dst_num_blocks) return PKV_ERR_SHAPE;
+  }
+  const size_t block_bytes = (size_t)block_size * num_heads * head_dim * sizeof(uint16_t);
+  // Staging: [the scatter mapping of every pair, 256-byte aligned][K slots]
+  // [V slots]; the mapping goes up once, the slots are reused chunk by chunk.
+  const size_t map_bytes = ((size_t)num_pairs * 2 * sizeof(int32_t) + 255) & ~(size_t)255;
+  if (staging_bytes < map_bytes + 2 * block_bytes) return PKV_ERR_WORKSPACE;
+  const int cap = (int)std::min<size_t>((staging_bytes - map_bytes) / (2 * block_bytes),
+                                        (size_t)num_pairs);
+  const void *sk, *sv, *dk, *dv, *stg;
+  if ((rc = device_accessible(src_key, block_bytes * src_num_blocks, &sk)) ||
+      (rc = device_accessible(src_value, block_bytes * src_num_blocks, &sv)) ||
+      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk)) ||
+      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv)) ||
+      (rc = device_accessible(staging, map_bytes + 2 * (size_t)cap * block_bytes, &stg)))
+    return rc;
+  char* st_map = static_cast<char*>(const_cast<void*>(stg));
+  char* st_k = st_map + map_bytes;
+  char* st_v = st_k + (size_t)cap * block_bytes;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Scatter mapping: pair i moves staging slot i % cap to its destination.
+  std::vector<int32_t> scatter(2 * (size_t)num_pairs);
+  for (int i = 0; i < num_pairs; ++i) {
+    scatter[2 * i] = i % cap;
+    scatter[2 * i + 1] = block_mapping[2 * i + 1];
+  }
+  if (hipMemcpyAsync(st_map, scatter.data(), scatter.size() * sizeof(int32_t),
+                     hipMemcpyHostToDevice, st) != hipSuccess)
+    return PKV_ERR_LAUNCH;
+  for (int c0 = 0; c0 < num_pairs; c0 += cap) {
+    const int n = std::min(cap, num_pairs - c0);
+    // DMA: each run of consecutive source ids into consecutive staging slots.
+    for (int i = 0; i < n;) {
+      const int32_t s0 = block_mapping[2 * (c0 + i)];
+      int r = 1;
+      while (i + r < n && block_mapping[2 * (c0 + i + r)] == s0 + r) ++r;
+      const size_t bytes = block_bytes * (size_t)r;
+      const size_t so = block_bytes * (size_t)s0, to = block_bytes * (size_t)i;
+      if (hipMemcpyAsync(st_k + to, static_cast<const char*>(sk) + so, bytes, hipMemcpyDefault,
+                         st) != hipSuccess ||
+          hipMemcpyAsync(st_v + to, static_cast<const char*>(sv) + so, bytes, hipMemcpyDefault,
+                         st) != hipSuccess)
+        return PKV_ERR_LAUNCH;
+      i += r;
+    }
+    // Scatter: staging slot -> destination block, one kernel launch per chunk.
+    rc = status_of(pkv::launch_copy_blocks(st_k, st_v, const_cast<void*>(dk),
+                                           const_cast<void*>(dv),
+                                           reinterpret_cast<const int32_t*>(st_map) + 2 * c0, n,
+                                           (int64_t)block_size * num_heads * head_dim,
+                                           /*system_release=*/true, st));
+    if (rc) return rc;
   }
   return PKV_OK;
 }

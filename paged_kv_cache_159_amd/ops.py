@@ -251,18 +251,24 @@ def _pool_tensor(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, method: str = "kernel"):
+def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, method: str = "kernel",
+                staging=None):
     """Copy whole blocks src -> dst from the (src_key, src_value) pools into the
     (dst_key, dst_value) pools, one of which lives in pinned host memory:
     swap-out (device -> host) or swap-in (host -> device), on the current
     stream of the GPU involved.
     method "kernel": one launch; ``block_mapping`` int32 [P, 2] on that GPU or
     pinned. method "dma": DMA copies per run of consecutive blocks;
-    ``block_mapping`` int32 [P, 2] on the CPU (read during the call)."""
-    if method not in ("kernel", "dma"):
-        raise ValueError("method must be 'kernel' or 'dma'")
-    if method == "dma" and block_mapping.device.type != "cpu":
-        raise ValueError("method 'dma' reads block_mapping on the host: pass a CPU tensor")
+    ``block_mapping`` int32 [P, 2] on the CPU (read during the call).
+    method "staged": DMA of runs of consecutive source blocks into ``staging``
+    (a uint8 GPU tensor), then one scatter launch per chunk; mapping on the
+    CPU."""
+    if method not in ("kernel", "dma", "staged"):
+        raise ValueError("method must be 'kernel', 'dma' or 'staged'")
+    if method != "kernel" and block_mapping.device.type != "cpu":
+        raise ValueError(f"method '{method}' reads block_mapping on the host: pass a CPU tensor")
+    if method == "staged" and (staging is None or staging.device.type != "cuda"):
+        raise ValueError("method 'staged' needs a GPU staging tensor")
     for t, n in ((src_key, "src_key"), (src_value, "src_value"), (dst_key, "dst_key"),
                  (dst_value, "dst_value")):
         _pool_tensor(t, n)
@@ -285,9 +291,13 @@ def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, method: s
     if len(gpus) != 1:
         raise ValueError("exactly one GPU must be involved")
     dev = next(iter(gpus))
-    fn = "swap_blocks" if method == "kernel" else "swap_blocks_dma"
-    rc = getattr(lib(), fn)(src_key.data_ptr(), src_value.data_ptr(), dst_key.data_ptr(),
-                            dst_value.data_ptr(), block_mapping.data_ptr(),
-                            block_mapping.shape[0], H, D, NBs, NBd, bs, dt,
-                            torch.cuda.current_stream(dev).cuda_stream)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    args = (src_key.data_ptr(), src_value.data_ptr(), dst_key.data_ptr(), dst_value.data_ptr(),
+            block_mapping.data_ptr(), block_mapping.shape[0], H, D, NBs, NBd, bs, dt)
+    if method == "staged":
+        fn = "swap_blocks_staged"
+        rc = lib().swap_blocks_staged(*args, staging.data_ptr(), staging.numel(), st)
+    else:
+        fn = "swap_blocks" if method == "kernel" else "swap_blocks_dma"
+        rc = getattr(lib(), fn)(*args, st)
     check(fn, rc)

@@ -303,3 +303,30 @@ def test_swap_blocks_dma_validation(L):
     a[4], a[5] = ctypes.addressof(bad), 1
     assert f(*a) == SHAPE                          # negative id
     assert f(*base) == MEMORY                      # ids fine, pools are fake
+
+
+def test_swap_blocks_staged_validation(L):
+    """Host-side checks before any HIP call: ids, the staging buffer's size
+    and alignment; valid arguments with fake pools stop at the memory check."""
+    f = L.swap_blocks_staged
+    m = (ctypes.c_int32 * 6)(0, 1, 1, 2, 7, 3)
+    mp = ctypes.addressof(m)
+    block_bytes = 16 * 4 * 64 * 2
+    big = 256 + 10 * 2 * block_bytes
+    base = [P, P, P, P, mp, 3, 4, 64, 8, 4, 16, 0, 0x20000, big, 0]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(11, 3) == UNSUP
+    assert call(10, 12) == UNSUP
+    assert call(5, -1) == SHAPE
+    for i in (0, 1, 2, 3, 4, 12):
+        assert call(i, 0) == NULL, i
+    assert call(12, 0x20000 + 16) == ALIGN        # staging must be 256-byte aligned
+    assert call(8, 7) == SHAPE                    # source id 7 outside a 7-block pool
+    assert call(13, 256 + 2 * block_bytes - 1) == WS
+    assert call(5, 0) == OK
+    assert f(*base) == MEMORY

@@ -422,7 +422,8 @@ def _pairs(arrays):
     return np.concatenate(arrays).astype(np.int32).reshape(-1, 2)
 
 
-@pytest.mark.parametrize("bs,method", [(16, "kernel"), (8, "kernel"), (16, "dma"), (32, "dma")])
+@pytest.mark.parametrize("bs,method", [(16, "kernel"), (8, "kernel"), (16, "dma"), (32, "dma"),
+                                       (16, "staged"), (8, "staged")])
 def test_swap_out_and_in_round_trip(bs, method):
     """16 sequences of the llama7b decode batch are swapped out to pinned host
     pools (one launch), their freed device blocks are overwritten with NaN,
@@ -434,6 +435,10 @@ def test_swap_out_and_in_round_trip(bs, method):
     w = make_config(2, bs)
     say(f"swap round trip: {method} bs={bs} S={w.num_seqs} NB={w.num_blocks}")
     as_map = (lambda p: torch.from_numpy(p).cuda()) if method == "kernel" else torch.from_numpy
+    # staged: a buffer of 40 pairs, so the swaps run in several chunks
+    block_bytes = w.block_size * w.num_heads * w.head_dim * 2
+    staging = (torch.empty(4096 + 40 * 2 * block_bytes, dtype=torch.uint8, device="cuda")
+               if method == "staged" else None)
     dw = upload(w)
     gpu_step(w, dw)
     before = device_to_bits(dw.out)
@@ -446,7 +451,8 @@ def test_swap_out_and_in_round_trip(bs, method):
     hk0, hv0 = device_to_bits(hk).copy(), device_to_bits(hv).copy()   # snapshots, not views
     dev_k, dev_v = device_to_bits(dw.key_cache), device_to_bits(dw.value_cache)
     out_pairs = _pairs([sw.swap_out(s) for s in seqs])
-    pkv.swap_blocks(dw.key_cache, dw.value_cache, hk, hv, as_map(out_pairs), method=method)
+    pkv.swap_blocks(dw.key_cache, dw.value_cache, hk, hv, as_map(out_pairs), method=method,
+                    staging=staging)
     torch.cuda.synchronize()
     HK, HV = oracle.swap_blocks(dev_k, dev_v, hk0, hv0, out_pairs)
     assert np.array_equal(device_to_bits(hk), HK) and np.array_equal(device_to_bits(hv), HV)
@@ -457,7 +463,8 @@ def test_swap_out_and_in_round_trip(bs, method):
     dw.value_cache[free] = nan
     dev_k2, dev_v2 = device_to_bits(dw.key_cache), device_to_bits(dw.value_cache)
     in_pairs = _pairs([sw.swap_in(s) for s in seqs])
-    pkv.swap_blocks(hk, hv, dw.key_cache, dw.value_cache, as_map(in_pairs), method=method)
+    pkv.swap_blocks(hk, hv, dw.key_cache, dw.value_cache, as_map(in_pairs), method=method,
+                    staging=staging)
     torch.cuda.synchronize()
     K3, V3 = oracle.swap_blocks(HK, HV, dev_k2, dev_v2, in_pairs)
     assert np.array_equal(device_to_bits(dw.key_cache), K3)
