@@ -99,8 +99,12 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   constexpr int PIECES = kPrefillKeys * D / 8;    // 16-byte pieces of K (or V) per stage
   constexpr int PER_THREAD = PIECES / THREADS;
   static_assert(PIECES % THREADS == 0, "whole pieces per thread");
-  __shared__ __align__(16) uint8_t s_k[kPrefillKeys * KROW];
-  __shared__ __align__(16) uint8_t s_vt[D * kVtRow];
+#ifndef PKV_PREFILL_DBUF
+#define PKV_PREFILL_DBUF 1
+#endif
+  constexpr int NBUF = PKV_PREFILL_DBUF ? 2 : 1;
+  __shared__ __align__(16) uint8_t s_kbuf[NBUF][kPrefillKeys * KROW];
+  __shared__ __align__(16) uint8_t s_vtbuf[NBUF][D * kVtRow];
 
   const int H = num_heads;
   const int h = blockIdx.x % H;
@@ -159,7 +163,9 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       pv[it] = *reinterpret_cast<const uint4*>(value_cache + off);
     }
   };
-  auto store_stage = [&]() {
+  auto store_stage = [&](int buf) {
+    uint8_t* s_k = s_kbuf[buf];
+    uint8_t* s_vt = s_vtbuf[buf];
 #pragma unroll
     for (int it = 0; it < PER_THREAD; ++it) {
       const int q = threadIdx.x + it * THREADS;
@@ -176,12 +182,21 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
 
   const int nstages = (nkeys + kPrefillKeys - 1) / kPrefillKeys;
   load_stage(0);
-  for (int st = 0; st < nstages; ++st) {
-    __syncthreads();                  // every wave is done with the previous stage
-    store_stage();
+  if constexpr (NBUF == 2) {
+    store_stage(0);
     __syncthreads();
-    if (st + 1 < nstages) load_stage(st + 1);
-    if (wrow0 >= qn) continue;        // a wave past the chunk's end only helps staging
+    if (nstages > 1) load_stage(1);
+  }
+  for (int st = 0; st < nstages; ++st) {
+    if constexpr (NBUF == 1) {
+      __syncthreads();                // every wave is done with the previous stage
+      store_stage(0);
+      __syncthreads();
+      if (st + 1 < nstages) load_stage(st + 1);
+    }
+    const uint8_t* s_k = s_kbuf[NBUF == 2 ? (st & 1) : 0];
+    const uint8_t* s_vt = s_vtbuf[NBUF == 2 ? (st & 1) : 0];
+    if (wrow0 < qn) {                 // a wave past the chunk's end only helps staging
 #pragma unroll
     for (int kp = 0; kp < kPrefillKeys / 32; ++kp) {
       const int kbase = st * kPrefillKeys + kp * 32;     // first key of this 32-key step
@@ -252,6 +267,14 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           acc[j][c] = t;
         }
       }
+    }
+    }
+    if constexpr (NBUF == 2) {
+      // The other buffer was last read in stage st - 1; every wave has
+      // passed the barrier that ended it.
+      if (st + 1 < nstages) store_stage((st + 1) & 1);
+      __syncthreads();
+      if (st + 2 < nstages) load_stage(st + 2);
     }
   }
 
