@@ -222,8 +222,17 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         float x[8];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          x[v] = (kbase + 4 * grp + v <= qpos) ? sa[v] * scale_log2 : -INFINITY;
-          x[4 + v] = (kbase + 16 + 4 * grp + v <= qpos) ? sb[v] * scale_log2 : -INFINITY;
+          x[v] = sa[v] * scale_log2;
+          x[4 + v] = sb[v] * scale_log2;
+        }
+        // Only steps reaching past the tile's first query position need the
+        // causal mask (wave-uniform test).
+        if (kbase + 31 > first + wrow0 + 16 * j) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (kbase + 4 * grp + v > qpos) x[v] = -INFINITY;
+            if (kbase + 16 + 4 * grp + v > qpos) x[4 + v] = -INFINITY;
+          }
         }
         float bm = x[0];
 #pragma unroll
