@@ -149,7 +149,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   // Piece it of this thread: key row r = q / (D/8) of the stage, 16-byte
   // column cc = q % (D/8), q = threadIdx.x + it * THREADS. Keys past the
   // last needed one re-read it (valid, a cache hit); the mask drops them.
-  uint4 pk[PER_THREAD], pv[PER_THREAD];
+  // Native 4-lane vectors: the compiler keeps them in registers across the
+  // stage loop (HIP's struct uint4 here ended up in scratch memory, which made
+  // every stage wait for its K loads as soon as they were issued).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 pk[PER_THREAD], pv[PER_THREAD];
   auto load_stage = [&](int st) {
 #pragma unroll
     for (int it = 0; it < PER_THREAD; ++it) {
@@ -159,8 +163,8 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       const int kpos = min(st * kPrefillKeys + r, nkeys - 1);
       const size_t slot = (size_t)bt[kpos / BS] * BS + (kpos % BS);
       const size_t off = slot * kv_dim + (size_t)h * D + cc * 8;
-      pk[it] = *reinterpret_cast<const uint4*>(key_cache + off);
-      pv[it] = *reinterpret_cast<const uint4*>(value_cache + off);
+      pk[it] = *reinterpret_cast<const u32x4*>(key_cache + off);
+      pv[it] = *reinterpret_cast<const u32x4*>(value_cache + off);
     }
   };
   auto store_stage = [&](int buf) {
@@ -171,8 +175,8 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       const int q = threadIdx.x + it * THREADS;
       const int r = q / (D / 8);
       const int cc = q % (D / 8);
-      *reinterpret_cast<uint4*>(s_k + r * KROW + cc * 16) = pk[it];
-      const uint32_t w[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w};
+      *reinterpret_cast<u32x4*>(s_k + r * KROW + cc * 16) = pk[it];
+      const u32x4 w = pv[it];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * kVtRow + vt_key_offset(cc * 8 + e, r)) =
