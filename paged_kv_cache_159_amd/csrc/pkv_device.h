@@ -25,6 +25,7 @@ __host__ __device__ __forceinline__ int shared_prefix_tokens(int shared_blocks, 
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 struct F16 {};
 struct BF16 {};
@@ -49,6 +50,10 @@ template <> struct Elem<F16> {
   static __device__ __forceinline__ uint16_t round(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
   }
+  // round(a) in the low half, round(b) in the high half (one packed convert).
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, half2_t));
+  }
 };
 
 template <> struct Elem<BF16> {
@@ -61,6 +66,9 @@ template <> struct Elem<BF16> {
   static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
   static __device__ __forceinline__ uint16_t round(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, bf162_t));
   }
 };
 

@@ -17,20 +17,26 @@
 // are dispatched last-first (the causal work of a tile grows with its
 // position). Keys are staged through LDS 64 at a time, gathered row by row
 // through the block table (any block size): K row-major (rows padded by 16
-// bytes), V transposed (V^T[dim][key], so an MFMA operand of 4 consecutive
-// keys of one dim is one 8-byte read). The next stage's rows are held in
-// registers while the waves compute on the current one.
+// bytes), V transposed (V^T[dim][key]). At head size 128 the transpose runs
+// in registers (a 4 x 4 word exchange across lane groups) and each lane
+// stores two 16-byte V^T pieces; other head sizes store 2-byte elements. The
+// next stage's rows are held in registers while the waves compute on the
+// current one, in a second LDS buffer (one barrier per stage).
 //
 // Arithmetic, per 32 keys and 16 queries:
 //   S^T = K Q^T with v_mfma_f32_16x16x32 (A = 16 key rows, B = the queries'
 //   rows), two 16-key tiles; the accumulator holds S^T[key 4g+v][query l%16].
-//   Causal mask (key position > query position -> -inf), online softmax per
-//   query column in the log2 domain (max and sum across the 4 lane groups by
-//   gfx950's row-swap instructions).
+//   Causal mask (key position > query position -> -inf; only on steps that
+//   reach past the wave's first query), online softmax per query column in
+//   the log2 domain (max and sum across the 4 lane groups by gfx950's
+//   row-swap instructions), against a reference that moves only when a score
+//   exceeds it by more than 2^8, so most steps skip the rescale.
 //   O^T += V^T P^T with one v_mfma_f32_16x16x32 per 16 output dims: its K index
 //   8g+e runs over keys 4g+e of the first tile (e < 4) and 16+4g+(e-4) of the
 //   second, which is exactly where the two S^T accumulators already hold P^T,
-//   so P never moves between lanes; V^T's operand is two 8-byte LDS reads.
+//   so P never moves between lanes; V^T's operand is one 16-byte LDS read
+//   at head size 128 (the two 4-key groups stored side by side), two 8-byte
+//   reads otherwise.
 //   fp16: P is rounded once to fp16 (11-bit significand; the sum l stays
 //   fp32). bf16: rounding P to bf16's 8 bits made ~0.1% of outputs miss half
 //   an output ulp against the exact result, so P is split into hi + lo bf16
@@ -80,7 +86,34 @@ __device__ __forceinline__ int vt_key_offset(int d, int k) {
 template <int D>
 constexpr int prefill_krow() { return 2 * D + 16; }
 
+// Paired V^T layout (head size 128, 64-key stages, 8 waves). The P.V operand
+// of one lane is 8 keys of one dim: keys 4g..4g+3 and 16+4g..16+4g+3 of a
+// 32-key step (lane group g). They sit side by side as one 16-byte unit
+// u = 4 * step + g of the dim's row, so an operand is one 16-byte read. A row
+// is 8 units plus 16 bytes of padding, and unit u of row d is stored at
+// u ^ ((d >> 4) & 7). Reads (16 consecutive dims, one unit) and the stores
+// below (16 column pieces, one unit) then fall on distinct LDS banks.
+constexpr int kPairedVtRow = 8 * 16 + 16;
+
+// 4 x 4 transpose of 32-bit words across the lane groups (lanes l, l + 16,
+// l + 32, l + 48): afterwards word k of lane group g is word g of lane group
+// k. v_permlane32_swap exchanges the upper half of its first operand with
+// the lower half of its second; v_permlane16_swap the odd 16-lane rows of its
+// first operand with the even rows of its second.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lane_group_transpose4(u32x4_t& x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x = u32x4_t{c[0], c[1], e[0], e[1]};
+}
+
 int prefill_rows_per_tile() { return kPrefillRows; }
+
+// Largest log2 gap between a step's max score and the softmax reference that
+// keeps the reference (weights then stay at most 2^8).
+constexpr float kRefSlack = 8.f;
 
 template <typename T, int D, int BS>
 __global__ void __launch_bounds__(kPrefillWaves * 64)
@@ -104,7 +137,9 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
 #endif
   constexpr int NBUF = PKV_PREFILL_DBUF ? 2 : 1;
   __shared__ __align__(16) uint8_t s_kbuf[NBUF][kPrefillKeys * KROW];
-  __shared__ __align__(16) uint8_t s_vtbuf[NBUF][D * kVtRow];
+  constexpr bool kPaired = D == 128 && kPrefillKeys == 64 && kPrefillWaves == 8;
+  constexpr int VTROW = kPaired ? kPairedVtRow : kVtRow;
+  __shared__ __align__(16) uint8_t s_vtbuf[NBUF][D * VTROW];
 
   const int H = num_heads;
   const int h = blockIdx.x % H;
@@ -152,14 +187,33 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   // Native 4-lane vectors: the compiler keeps them in registers across the
   // stage loop (HIP's struct uint4 here ended up in scratch memory, which made
   // every stage wait for its K loads as soon as they were issued).
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef u32x4_t u32x4;
   u32x4 pk[PER_THREAD], pv[PER_THREAD];
+  // Piece it of this thread: key row r of the stage, 16-byte column piece cc.
+  // Plain layout: q = threadIdx.x + it * THREADS, r = q / (D/8), cc = q % (D/8).
+  // Paired layout: wave w reads key groups 4 * kg .. 4 * kg + 3 with
+  // kg = 8 * (w / 4) + w % 4 + 4 * it (the two halves of unit w), lane group g
+  // the key 4 * kg + g, and the 16 lanes of a group the pieces of that key
+  // row in the order cc = 2 * (l % 8) + (l / 8) % 2.
+  auto piece_row = [&](int it) {
+    if constexpr (kPaired)
+      return 4 * (8 * (wave >> 2) + (wave & 3) + 4 * it) + (lane >> 4);
+    else
+      return (int)(threadIdx.x + it * THREADS) / (D / 8);
+  };
+  auto piece_col = [&](int it) {
+    if constexpr (kPaired)
+      return ((lane & 7) << 1) | ((lane >> 3) & 1);
+    else
+      return (int)(threadIdx.x + it * THREADS) % (D / 8);
+  };
+  // Keys past the last needed one re-read it (valid, a cache hit); the mask
+  // drops them.
   auto load_stage = [&](int st) {
 #pragma unroll
     for (int it = 0; it < PER_THREAD; ++it) {
-      const int q = threadIdx.x + it * THREADS;
-      const int r = q / (D / 8);
-      const int cc = q % (D / 8);
+      const int r = piece_row(it);
+      const int cc = piece_col(it);
       const int kpos = min(st * kPrefillKeys + r, nkeys - 1);
       const size_t slot = (size_t)bt[kpos / BS] * BS + (kpos % BS);
       const size_t off = slot * kv_dim + (size_t)h * D + cc * 8;
@@ -171,16 +225,36 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     uint8_t* s_k = s_kbuf[buf];
     uint8_t* s_vt = s_vtbuf[buf];
 #pragma unroll
-    for (int it = 0; it < PER_THREAD; ++it) {
-      const int q = threadIdx.x + it * THREADS;
-      const int r = q / (D / 8);
-      const int cc = q % (D / 8);
-      *reinterpret_cast<u32x4*>(s_k + r * KROW + cc * 16) = pk[it];
-      const u32x4 w = pv[it];
+    for (int it = 0; it < PER_THREAD; ++it)
+      *reinterpret_cast<u32x4*>(s_k + piece_row(it) * KROW + piece_col(it) * 16) = pk[it];
+    if constexpr (kPaired) {
+      // After the transpose, word k of piece it holds dims (2g, 2g + 1) of
+      // the column piece for key 4 * kg + k: dim 8 cc + 2g gets the low
+      // halves, dim 8 cc + 2g + 1 the high halves, 8 keys each (one unit).
+      u32x4 x0 = pv[0], x1 = pv[1];
+      lane_group_transpose4(x0);
+      lane_group_transpose4(x1);
+      const int cc = piece_col(0);
+      const int d = cc * 8 + 2 * (lane >> 4);
+      const int unit = 16 * (wave ^ ((d >> 4) & 7));     // d and d + 1 share d >> 4
+      const u32x4 lo = {(x0[0] & 0xffffu) | (x0[1] << 16), (x0[2] & 0xffffu) | (x0[3] << 16),
+                        (x1[0] & 0xffffu) | (x1[1] << 16), (x1[2] & 0xffffu) | (x1[3] << 16)};
+      const u32x4 hi = {(x0[0] >> 16) | (x0[1] & 0xffff0000u), (x0[2] >> 16) | (x0[3] & 0xffff0000u),
+                        (x1[0] >> 16) | (x1[1] & 0xffff0000u), (x1[2] >> 16) | (x1[3] & 0xffff0000u)};
+      *reinterpret_cast<u32x4*>(s_vt + d * VTROW + unit) = lo;
+      *reinterpret_cast<u32x4*>(s_vt + (d + 1) * VTROW + unit) = hi;
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * kVtRow + vt_key_offset(cc * 8 + e, r)) =
-            (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      for (int it = 0; it < PER_THREAD; ++it) {
+        const int r = piece_row(it);
+        const int cc = piece_col(it);
+        const u32x4 w = pv[it];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * VTROW +
+                                       vt_key_offset(cc * 8 + e, r)) =
+              (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
     }
   };
 
@@ -206,80 +280,124 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       const int kbase = st * kPrefillKeys + kp * 32;     // first key of this 32-key step
       if (kbase > wave_last_pos) break;                  // wave-uniform
       const int lk = kp * 32;
-      uint4 ka[NK], kb[NK];
-#pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        ka[i] = *reinterpret_cast<const uint4*>(s_k + (lk + col) * KROW + (32 * i + 8 * grp) * 2);
-        kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * KROW +
-                                                (32 * i + 8 * grp) * 2);
-      }
-#pragma unroll
-      for (int j = 0; j < QW; ++j) {
-        if (wrow0 + 16 * j >= qn) continue;              // wave-uniform
-        const int qpos = first + wrow0 + 16 * j + col;   // this lane's query position
-        f4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      // One 32-key step for all QW query tiles, as one branch-free block: the
+      // S^T products of every tile first, then the softmax updates, then the
+      // P.V products, so one tile's VALU work can overlap another's MFMAs.
+      // Rows past the chunk's end (zero queries) are computed and dropped at
+      // the store. Only steps reaching past the wave's first query position
+      // take the causal mask (instantiated apart, so the others skip it).
+      auto step = [&](auto mask_tag) {
+        constexpr bool kMask = decltype(mask_tag)::value;
+        uint4 ka[NK], kb[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-          sa = M::k32(ka[i], qf[j][i], sa);
-          sb = M::k32(kb[i], qf[j][i], sb);
+          ka[i] = *reinterpret_cast<const uint4*>(s_k + (lk + col) * KROW + (32 * i + 8 * grp) * 2);
+          kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * KROW +
+                                                  (32 * i + 8 * grp) * 2);
         }
-        float x[8];
+        f4_t sa[QW], sb[QW];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          x[v] = sa[v] * scale_log2;
-          x[4 + v] = sb[v] * scale_log2;
-        }
-        // Only steps reaching past the tile's first query position need the
-        // causal mask (wave-uniform test).
-        if (kbase + 31 > first + wrow0 + 16 * j) {
+        for (int j = 0; j < QW; ++j) {
+          sa[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+          sb[j] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            if (kbase + 4 * grp + v > qpos) x[v] = -INFINITY;
-            if (kbase + 16 + 4 * grp + v > qpos) x[4 + v] = -INFINITY;
+          for (int i = 0; i < NK; ++i) {
+            sa[j] = M::k32(ka[i], qf[j][i], sa[j]);
+            sb[j] = M::k32(kb[i], qf[j][i], sb[j]);
           }
         }
-        float bm = x[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, x[e]);
-        bm = lane_group4_max(bm);
-        // The first step holds key 0, which every query sees, so m is finite
-        // from then on; a later step whose keys are all masked for a query
-        // leaves it unchanged (alpha = 1, p = 0).
-        const float mn = fmaxf(m[j], bm);
-        const float alpha = fast_exp2(m[j] - mn);
-        float p[8], ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(x[e] - mn);
-          ps += p[e];
-        }
-        ps = lane_group4_sum(ps);
-        l[j] = l[j] * alpha + ps;
-        m[j] = mn;
         constexpr bool kSplit = std::is_same<T, BF16>::value;
-        uint32_t hi[8], lo[8];
+        uint4 bhi[QW], blo[QW];
+        float mnew[QW], psum[QW];
+        bool moved = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi[e] = E::round(p[e]);
-          lo[e] = kSplit ? E::round(p[e] - M::widen(hi[e])) : 0u;
+        for (int j = 0; j < QW; ++j) {
+          // Scaled scores in the log2 domain (products are canonical floats,
+          // so the max below needs no quieting of its inputs).
+          float x[8];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            x[v] = sa[j][v] * scale_log2;
+            x[4 + v] = sb[j][v] * scale_log2;
+          }
+          if constexpr (kMask) {
+            const int qpos = first + wrow0 + 16 * j + col;   // this lane's query position
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              if (kbase + 4 * grp + v > qpos) x[v] = -INFINITY;
+              if (kbase + 16 + 4 * grp + v > qpos) x[4 + v] = -INFINITY;
+            }
+          }
+          float bm = x[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) bm = fmaxf(bm, x[e]);
+          bm = lane_group4_max(bm);
+          // Reference for the weights: raised to the step's max only when
+          // that exceeds it by more than kRefSlack (log2 units), so every
+          // weight stays at most 2^kRefSlack, well inside the 16-bit range.
+          // Softmax does not depend on the reference, and most steps keep
+          // it, which skips the rescale of the accumulators below. The first
+          // step holds key 0, which every query sees, so the reference is
+          // finite from then on; a step whose keys are all masked for a
+          // query keeps it.
+          mnew[j] = (bm > m[j] + kRefSlack) ? bm : m[j];
+          moved |= mnew[j] != m[j];
+          const float nm = -mnew[j];
+          float p[8], ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] + nm);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ps += p[e];
+          psum[j] = lane_group4_sum(ps);
+          uint32_t hi[4], lo[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = E::pack2(p[2 * e], p[2 * e + 1]);
+            if constexpr (kSplit)
+              lo[e] = E::pack2(p[2 * e] - M::widen(hi[e] & 0xffffu), p[2 * e + 1] - M::widen(hi[e] >> 16));
+          }
+          bhi[j] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          blo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
-        const uint4 bhi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                     hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-        const uint4 blo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                     lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+        if (__builtin_expect(__any(moved), 0)) {         // wave-uniform, rare
+#pragma unroll
+          for (int j = 0; j < QW; ++j) {
+            const float alpha = fast_exp2(m[j] - mnew[j]);  // exactly 1 where kept
+            l[j] *= alpha;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[j][c] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+          l[j] += psum[j];
+          m[j] = mnew[j];
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int d = 16 * c + col;
-          const uint8_t* vrow = s_vt + d * kVtRow;
-          const uint2 va = *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 4 * grp));
-          const uint2 vb =
-              *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 16 + 4 * grp));
-          const uint4 a = make_uint4(va.x, va.y, vb.x, vb.y);
-          f4_t t = M::k32(a, bhi, acc[j][c] * alpha);
-          if constexpr (kSplit) t = M::k32(a, blo, t);
-          acc[j][c] = t;
+          const uint8_t* vrow = s_vt + d * VTROW;
+          uint4 a;
+          if constexpr (kPaired) {
+            a = *reinterpret_cast<const uint4*>(vrow + 16 * ((kp * 4 + grp) ^ (c & 7)));
+          } else {
+            const uint2 va = *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 4 * grp));
+            const uint2 vb =
+                *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 16 + 4 * grp));
+            a = make_uint4(va.x, va.y, vb.x, vb.y);
+          }
+#pragma unroll
+          for (int j = 0; j < QW; ++j) {
+            f4_t t = M::k32(a, bhi[j], acc[j][c]);
+            if constexpr (kSplit) t = M::k32(a, blo[j], t);
+            acc[j][c] = t;
+          }
         }
-      }
+      };
+      if (kbase + 31 > first + wrow0)
+        step(std::true_type{});
+      else
+        step(std::false_type{});
     }
     }
     if constexpr (NBUF == 2) {
