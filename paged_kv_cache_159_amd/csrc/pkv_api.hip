@@ -107,7 +107,7 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
 
 // Partial slots of the grouped call: shared-prefix chunks, then tail partitions.
 void grouped_slots(int max_blocks_per_seq, int block_size, int* chunk_slots, int* tail_parts) {
-  // shared tokens <= max_blocks_per_seq * block_size, in chunks of 8 tiles of 16
+  // shared tokens <= max_blocks_per_seq * block_size, in chunks of kSharedChunkTiles tiles of 16
   constexpr int64_t chunk_tokens = pkv::kSharedChunkTiles * pkv::kTileTokens;
   *chunk_slots = (int)(((int64_t)max_blocks_per_seq * block_size + chunk_tokens - 1) / chunk_tokens);
   *tail_parts = num_partitions(max_blocks_per_seq, block_size);

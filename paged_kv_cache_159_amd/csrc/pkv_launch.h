@@ -12,7 +12,7 @@ namespace pkv {
 constexpr int kCopyVecsPerGroup = 1024;
 
 // Grouped decode: 16-token tiles of the shared prefix per shared-prefix unit
-// (128 tokens).
+// (128 tokens, streamed through LDS one tile at a time).
 constexpr int kSharedChunkTiles = 8;
 
 struct DecodeArgs {
