@@ -79,9 +79,10 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
 // slots [0, n0) and [slot_base, slot_base + n1) of the sequence's slot row
 // (the plain call uses only the first range; the grouped call puts the
 // shared-prefix chunks in the first and the tail partitions in the second).
-// 256 threads: thread (k, d) sums slots k, k + K, ... for output element d
-// (K = 256 / D), then the K partial sums meet in LDS (one barrier). The loads
-// of different slots are independent, so many are in flight.
+// 256 threads: thread (k, d) merges slots k, k + K, ... for output element d
+// (K = 256 / D) in one online pass, then the K states meet in LDS (one
+// barrier). The loads of different slots are independent, so many are in
+// flight.
 constexpr int kMergeThreads = 256;
 
 template <typename T, int D, bool GROUPED>
@@ -112,28 +113,43 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
   const size_t base = ((size_t)s * H + h) * num_parts;
   const int d = threadIdx.x % D;
   const int k = threadIdx.x / D;
-  // The maximum over all partials: the addresses are the same in every
-  // thread, so these are scalar loads and need no cross-thread reduction.
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, ws_ml[(base + slot(i)) * 2]);
-  float L = 0.f, o = 0.f;
-#pragma unroll 8
+  // One pass: each thread keeps a running (max, weight sum, output) over its
+  // partials, so a partial's (m, l) pair and output element are loaded
+  // together. Every partial covers at least one token, so its m is finite;
+  // the first one turns the running max from -inf into a number (weight
+  // 2^-inf = 0 for the empty state).
+  float M = -INFINITY, L = 0.f, o = 0.f;
+#pragma unroll 4
   for (int i = k; i < n; i += K) {
     const size_t pi = base + slot(i);
-    const float cw = ws_ml[pi * 2 + 1] * fast_exp2(ws_ml[pi * 2] - M);
-    L += cw;
-    o += cw * ws_o[pi * D + d];
+    const float mi = ws_ml[pi * 2];
+    const float li = ws_ml[pi * 2 + 1];
+    const float oi = ws_o[pi * D + d];
+    const float mn = fmaxf(M, mi);
+    const float a = fast_exp2(M - mn);
+    const float w = li * fast_exp2(mi - mn);
+    L = L * a + w;
+    o = o * a + w * oi;
+    M = mn;
   }
-  __shared__ float s_o[kMergeThreads], s_l[K];
+  __shared__ float s_o[kMergeThreads], s_m[K], s_l[K];
   s_o[threadIdx.x] = o;
-  if (d == 0) s_l[k] = L;
+  if (d == 0) {
+    s_m[k] = M;
+    s_l[k] = L;
+  }
   __syncthreads();
   if (k == 0) {
+    float mx = s_m[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) mx = fmaxf(mx, s_m[j]);
     float oo = 0.f, ll = 0.f;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      oo += s_o[j * D + d];
-      ll += s_l[j];
+      // a thread with no partials (n < K) holds M = -inf and weight 0
+      const float c = s_m[j] == -INFINITY ? 0.f : fast_exp2(s_m[j] - mx);
+      oo += s_o[j * D + d] * c;
+      ll += s_l[j] * c;
     }
     out[((size_t)s * H + h) * D + d] = E::round(oo / ll);
   }
