@@ -295,6 +295,10 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * KROW +
                                                   (32 * i + 8 * grp) * 2);
         }
+        // Wave priority: the softmax (a chain of dependent VALU work) runs
+        // at priority 1 and the MFMA blocks at 0, so on a SIMD the wave in
+        // its softmax wins issue slots while the other wave's MFMAs run.
+        __builtin_amdgcn_s_setprio(0);
         f4_t sa[QW], sb[QW];
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
@@ -310,6 +314,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         uint4 bhi[QW], blo[QW];
         float mnew[QW], psum[QW];
         bool moved = false;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
           // Scaled scores in the log2 domain (products are canonical floats,
@@ -373,6 +378,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           l[j] += psum[j];
           m[j] = mnew[j];
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int d = 16 * c + col;
@@ -393,6 +399,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
             acc[j][c] = t;
           }
         }
+        __builtin_amdgcn_s_setprio(1);
       };
       if (kbase + 31 > first + wrow0)
         step(std::true_type{});
