@@ -320,6 +320,22 @@ def test_grouped_large_groups_head_dim_64():
     check_grouped(make_shared_case(2, 20, 80, 0, 30, 3, 64, "f16", seed=5))
 
 
+@pytest.mark.parametrize("heads,head_dim,dtype", [(5, 128, "bf16"), (7, 128, "f16"), (6, 64, "f16")])
+def test_grouped_partial_head_groups(heads, head_dim, dtype):
+    """Head counts that leave the last shared-prefix unit's head group part
+    empty (units take 2 heads at head_dim 128, 4 at 64)."""
+    from workloads import make_shared_case
+    w = make_shared_case(3, 5, 96, 1, 40, heads, head_dim, dtype, seed=heads * head_dim)
+    check_grouped(w, format_bound="bf16" if dtype == "bf16" else None)
+
+
+def test_grouped_large_groups_head_dim_128():
+    """Groups of 21 (two 16-query tiles re-streaming the chunk), a prefix of
+    2.5 chunks, bf16 at head_dim 128."""
+    from workloads import make_shared_case
+    check_grouped(make_shared_case(2, 21, 330, 1, 50, 4, 128, "bf16", seed=9), format_bound="bf16")
+
+
 def test_grouped_fully_shared_no_tail():
     from workloads import make_shared_case
     w = make_shared_case(3, 4, 64, 0, 0, 4, 128, "bf16", seed=6)
