@@ -101,16 +101,22 @@ __device__ __forceinline__ float group_sum(float x) {
 // 2^x with the hardware instruction (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Group of sequence s: the g with group_start[g] <= s < group_start[g + 1]
-// (binary search; group_start is nondecreasing from 0 to num_seqs).
+// Group of sequence s: the largest g < num_groups with group_start[g] <= s
+// (group_start is nondecreasing from 0 to num_seqs, so that g has
+// group_start[g] <= s < group_start[g + 1], skipping empty groups). Called by
+// a whole wave with the same s: lane i loads group_start[i] of each 64-entry
+// chunk and the count of entries <= s comes from a ballot, so the lookup costs
+// one memory round trip per 64 groups instead of a chain of dependent loads.
 __device__ __forceinline__ int group_of(int s, const int32_t* __restrict__ group_start,
                                         int num_groups) {
-  int lo = 0, hi = num_groups;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (group_start[mid] <= s) lo = mid; else hi = mid;
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < num_groups; base += 64) {
+    const int g = base + lane;
+    const bool le = g < num_groups && group_start[g] <= s;
+    count += __popcll(__ballot(le));
   }
-  return lo;
+  return count > 0 ? count - 1 : 0;   // group_start[0] = 0, so count >= 1
 }
 
 }  // namespace pkv
