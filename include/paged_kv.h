@@ -260,7 +260,9 @@ int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping
  * hipPointerGetAttributes and hipMemGetAddressRange). One launch on `stream`
  * moves every pair; host memory is read and written by the kernel over the
  * host link, and the kernel's writes are visible to the host once `stream`
- * has been synchronised. Preconditions: src ids < src_num_blocks, dst ids <
+ * has been synchronised (when the destination pools are host memory, every
+ * workgroup ends with a system-scope release; device destinations need none).
+ * Preconditions: src ids < src_num_blocks, dst ids <
  * dst_num_blocks and unique. num_pairs == 0 is a no-op (pointers may then
  * be NULL).
  */

@@ -135,7 +135,7 @@ int check_grouped(int num_seqs, int num_heads, int head_dim, int block_size,
 // device memory of this device, or pinned (page-locked, mapped) host memory.
 // Anything else (pageable host memory, another device's memory, a range that
 // runs past its allocation) is refused with PKV_ERR_MEMORY before any launch.
-int device_accessible(const void* ptr, size_t bytes, const void** dev_ptr) {
+int device_accessible(const void* ptr, size_t bytes, const void** dev_ptr, bool* host = nullptr) {
   hipPointerAttribute_t attr;
   if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
     (void)hipGetLastError();  // clear the sticky error of the failed query
@@ -149,6 +149,7 @@ int device_accessible(const void* ptr, size_t bytes, const void** dev_ptr) {
   } else if (attr.type == hipMemoryTypeHost) {
     if (attr.devicePointer == nullptr) return PKV_ERR_MEMORY;
     *dev_ptr = attr.devicePointer;
+    if (host) *host = true;
   } else {
     return PKV_ERR_MEMORY;
   }
@@ -418,15 +419,18 @@ int swap_blocks(const void* src_key, const void* src_value, void* dst_key, void*
     return PKV_ERR_ALIGN;
   const size_t block_bytes = (size_t)block_elems * sizeof(uint16_t);
   const void *sk, *sv, *dk, *dv, *bm;
+  bool host_dst = false;
   if ((rc = device_accessible(src_key, block_bytes * src_num_blocks, &sk)) ||
       (rc = device_accessible(src_value, block_bytes * src_num_blocks, &sv)) ||
-      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk)) ||
-      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv)) ||
+      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk, &host_dst)) ||
+      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv, &host_dst)) ||
       (rc = device_accessible(block_mapping, (size_t)num_pairs * 2 * sizeof(int32_t), &bm)))
     return rc;
+  // The system-scope release (an L2 write-back in every workgroup) is needed
+  // only when the kernel writes pinned host memory.
   return status_of(pkv::launch_copy_blocks(sk, sv, const_cast<void*>(dk), const_cast<void*>(dv),
                                            static_cast<const int32_t*>(bm), num_pairs,
-                                           block_elems, true, static_cast<hipStream_t>(stream)));
+                                           block_elems, host_dst, static_cast<hipStream_t>(stream)));
 }
 
 
@@ -505,10 +509,11 @@ int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key
   const int cap = (int)std::min<size_t>((staging_bytes - map_bytes) / (2 * block_bytes),
                                         (size_t)num_pairs);
   const void *sk, *sv, *dk, *dv, *stg;
+  bool host_dst = false;
   if ((rc = device_accessible(src_key, block_bytes * src_num_blocks, &sk)) ||
       (rc = device_accessible(src_value, block_bytes * src_num_blocks, &sv)) ||
-      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk)) ||
-      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv)) ||
+      (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk, &host_dst)) ||
+      (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv, &host_dst)) ||
       (rc = device_accessible(staging, map_bytes + 2 * (size_t)cap * block_bytes, &stg)))
     return rc;
   char* st_map = static_cast<char*>(const_cast<void*>(stg));
@@ -545,7 +550,7 @@ int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key
                                            const_cast<void*>(dv),
                                            reinterpret_cast<const int32_t*>(st_map) + 2 * c0, n,
                                            (int64_t)block_size * num_heads * head_dim,
-                                           /*system_release=*/true, st));
+                                           /*system_release=*/host_dst, st));
     if (rc) return rc;
   }
   return PKV_OK;
