@@ -16,12 +16,14 @@
 // rows, head); each wave owns 32 query rows as two 16-column MFMA tiles. Tiles
 // are dispatched last-first (the causal work of a tile grows with its
 // position). Keys are staged through LDS 64 at a time, gathered row by row
-// through the block table (any block size): K row-major (rows padded by 16
-// bytes), V transposed (V^T[dim][key]). At head size 128 the transpose runs
-// in registers (a 4 x 4 word exchange across lane groups) and each lane
-// stores two 16-byte V^T pieces; other head sizes store 2-byte elements. The
-// next stage's rows are held in registers while the waves compute on the
-// current one, in a second LDS buffer (one barrier per stage).
+// through the block table (any block size), into two LDS buffers: the next
+// stage's rows arrive while the waves compute on the current one (one barrier
+// per stage). At head size 128 the rows go from global memory straight into
+// LDS (global_load_lds_dwordx4), K and V both row-major with XOR-swizzled
+// 16-byte pieces, and P.V reads its V^T operands with gfx950's transposing
+// LDS read (ds_read_b64_tr_b16). Other head sizes stage through registers:
+// K rows padded by 16 bytes, V transposed into V^T[dim][key] element by
+// element.
 //
 // Arithmetic, per 32 keys and 16 queries:
 //   S^T = K Q^T with v_mfma_f32_16x16x32 (A = 16 key rows, B = the queries'
@@ -34,9 +36,8 @@
 //   O^T += V^T P^T with one v_mfma_f32_16x16x32 per 16 output dims: its K index
 //   8g+e runs over keys 4g+e of the first tile (e < 4) and 16+4g+(e-4) of the
 //   second, which is exactly where the two S^T accumulators already hold P^T,
-//   so P never moves between lanes; V^T's operand is one 16-byte LDS read
-//   at head size 128 (the two 4-key groups stored side by side), two 8-byte
-//   reads otherwise.
+//   so P never moves between lanes; V^T's operand is two 8-byte LDS reads
+//   (transposing reads of the row-major V at head size 128).
 //   fp16: P is rounded once to fp16 (11-bit significand; the sum l stays
 //   fp32). bf16: rounding P to bf16's 8 bits made ~0.1% of outputs miss half
 //   an output ulp against the exact result, so P is split into hi + lo bf16
@@ -86,28 +87,7 @@ __device__ __forceinline__ int vt_key_offset(int d, int k) {
 template <int D>
 constexpr int prefill_krow() { return 2 * D + 16; }
 
-// Paired V^T layout (head size 128, 64-key stages, 8 waves). The P.V operand
-// of one lane is 8 keys of one dim: keys 4g..4g+3 and 16+4g..16+4g+3 of a
-// 32-key step (lane group g). They sit side by side as one 16-byte unit
-// u = 4 * step + g of the dim's row, so an operand is one 16-byte read. A row
-// is 8 units plus 16 bytes of padding, and unit u of row d is stored at
-// u ^ ((d >> 4) & 7). Reads (16 consecutive dims, one unit) and the stores
-// below (16 column pieces, one unit) then fall on distinct LDS banks.
-constexpr int kPairedVtRow = 8 * 16 + 16;
-
-// 4 x 4 transpose of 32-bit words across the lane groups (lanes l, l + 16,
-// l + 32, l + 48): afterwards word k of lane group g is word g of lane group
-// k. v_permlane32_swap exchanges the upper half of its first operand with
-// the lower half of its second; v_permlane16_swap the odd 16-lane rows of its
-// first operand with the even rows of its second.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void lane_group_transpose4(u32x4_t& x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  x = u32x4_t{c[0], c[1], e[0], e[1]};
-}
 
 int prefill_rows_per_tile() { return kPrefillRows; }
 
@@ -136,10 +116,23 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
 #define PKV_PREFILL_DBUF 1
 #endif
   constexpr int NBUF = PKV_PREFILL_DBUF ? 2 : 1;
-  __shared__ __align__(16) uint8_t s_kbuf[NBUF][kPrefillKeys * KROW];
-  constexpr bool kPaired = D == 128 && kPrefillKeys == 64 && kPrefillWaves == 8;
-  constexpr int VTROW = kPaired ? kPairedVtRow : kVtRow;
-  __shared__ __align__(16) uint8_t s_vtbuf[NBUF][D * VTROW];
+  // Direct staging (head size 128): K and V rows go from global memory
+  // straight into LDS (one 16-byte load per lane, lane l landing at the
+  // instruction's base + 16 l), unpadded 256-byte rows with XOR-swizzled
+  // 16-byte pieces; V stays row-major and P.V operands come from transposing
+  // LDS reads. Other head sizes stage through registers into padded K rows
+  // and a 2-byte-element V^T.
+  constexpr bool kDirect = D == 128 && kPrefillKeys == 64 && kPrefillWaves == 8;
+  constexpr int kDirectRow = 2 * D;                       // 256 bytes
+  constexpr int kDirectStage = 2 * kPrefillKeys * kDirectRow;   // K rows, then V rows
+  // Two separate arrays (not one indexed by the stage's parity), so the
+  // compiler can tell that the reads of one stage do not alias the loads in
+  // flight into the other and need not wait for them.
+  __shared__ __align__(16) uint8_t s_d0[kDirect ? kDirectStage : 16];
+  __shared__ __align__(16) uint8_t s_d1[kDirect ? kDirectStage : 16];
+  __shared__ __align__(16) uint8_t s_kbuf[kDirect ? 1 : NBUF][kDirect ? 16 : kPrefillKeys * KROW];
+  constexpr int VTROW = kVtRow;
+  __shared__ __align__(16) uint8_t s_vtbuf[kDirect ? 1 : NBUF][kDirect ? 16 : D * VTROW];
 
   const int H = num_heads;
   const int h = blockIdx.x % H;
@@ -189,24 +182,10 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   // every stage wait for its K loads as soon as they were issued).
   typedef u32x4_t u32x4;
   u32x4 pk[PER_THREAD], pv[PER_THREAD];
-  // Piece it of this thread: key row r of the stage, 16-byte column piece cc.
-  // Plain layout: q = threadIdx.x + it * THREADS, r = q / (D/8), cc = q % (D/8).
-  // Paired layout: wave w reads key groups 4 * kg .. 4 * kg + 3 with
-  // kg = 8 * (w / 4) + w % 4 + 4 * it (the two halves of unit w), lane group g
-  // the key 4 * kg + g, and the 16 lanes of a group the pieces of that key
-  // row in the order cc = 2 * (l % 8) + (l / 8) % 2.
-  auto piece_row = [&](int it) {
-    if constexpr (kPaired)
-      return 4 * (8 * (wave >> 2) + (wave & 3) + 4 * it) + (lane >> 4);
-    else
-      return (int)(threadIdx.x + it * THREADS) / (D / 8);
-  };
-  auto piece_col = [&](int it) {
-    if constexpr (kPaired)
-      return ((lane & 7) << 1) | ((lane >> 3) & 1);
-    else
-      return (int)(threadIdx.x + it * THREADS) % (D / 8);
-  };
+  // Piece it of this thread: q = threadIdx.x + it * THREADS is key row
+  // r = q / (D/8) of the stage, 16-byte column piece cc = q % (D/8).
+  auto piece_row = [&](int it) { return (int)(threadIdx.x + it * THREADS) / (D / 8); };
+  auto piece_col = [&](int it) { return (int)(threadIdx.x + it * THREADS) % (D / 8); };
   // Keys past the last needed one re-read it (valid, a cache hit); the mask
   // drops them.
   auto load_stage = [&](int st) {
@@ -227,53 +206,93 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
 #pragma unroll
     for (int it = 0; it < PER_THREAD; ++it)
       *reinterpret_cast<u32x4*>(s_k + piece_row(it) * KROW + piece_col(it) * 16) = pk[it];
-    if constexpr (kPaired) {
-      // After the transpose, word k of piece it holds dims (2g, 2g + 1) of
-      // the column piece for key 4 * kg + k: dim 8 cc + 2g gets the low
-      // halves, dim 8 cc + 2g + 1 the high halves, 8 keys each (one unit).
-      u32x4 x0 = pv[0], x1 = pv[1];
-      lane_group_transpose4(x0);
-      lane_group_transpose4(x1);
-      const int cc = piece_col(0);
-      const int d = cc * 8 + 2 * (lane >> 4);
-      const int unit = 16 * (wave ^ ((d >> 4) & 7));     // d and d + 1 share d >> 4
-      const u32x4 lo = {(x0[0] & 0xffffu) | (x0[1] << 16), (x0[2] & 0xffffu) | (x0[3] << 16),
-                        (x1[0] & 0xffffu) | (x1[1] << 16), (x1[2] & 0xffffu) | (x1[3] << 16)};
-      const u32x4 hi = {(x0[0] >> 16) | (x0[1] & 0xffff0000u), (x0[2] >> 16) | (x0[3] & 0xffff0000u),
-                        (x1[0] >> 16) | (x1[1] & 0xffff0000u), (x1[2] >> 16) | (x1[3] & 0xffff0000u)};
-      *reinterpret_cast<u32x4*>(s_vt + d * VTROW + unit) = lo;
-      *reinterpret_cast<u32x4*>(s_vt + (d + 1) * VTROW + unit) = hi;
-    } else {
 #pragma unroll
-      for (int it = 0; it < PER_THREAD; ++it) {
-        const int r = piece_row(it);
-        const int cc = piece_col(it);
-        const u32x4 w = pv[it];
+    for (int it = 0; it < PER_THREAD; ++it) {
+      const int r = piece_row(it);
+      const int cc = piece_col(it);
+      const u32x4 w = pv[it];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * VTROW +
-                                       vt_key_offset(cc * 8 + e, r)) =
-              (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-      }
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(s_vt + (cc * 8 + e) * VTROW +
+                                     vt_key_offset(cc * 8 + e, r)) =
+            (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   };
 
   const int nstages = (nkeys + kPrefillKeys - 1) / kPrefillKeys;
-  load_stage(0);
-  if constexpr (NBUF == 2) {
-    store_stage(0);
+  // Direct staging of stage st into buffer b: wave w issues 4 loads, each 4
+  // rows of K or V (64 lanes x 16 bytes). Lane l takes row r = r0 + l / 16 and
+  // LDS slot l % 16 of it, i.e. the row's piece (l % 16) ^ swizzle(r): K rows
+  // swizzle by r & 15 (16 consecutive rows read one piece column on distinct
+  // banks), V rows by 2 (r & 7) (the transposing reads take 8 rows x 2
+  // pieces at a time). A 16-lane row segment is one coalesced 256-byte read.
+  auto issue_stage = [&](int st, uint8_t* buf) {
+    // Table lookups and addresses of all four loads first, then the loads
+    // back to back (a lookup between them would wait for the loads before it).
+    const uint16_t* src[4];
+    uint32_t lds_base[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tensor = j >> 1;
+      const int r0 = 4 * (wave + 8 * (j & 1));
+      const int r = r0 + (lane >> 4);
+      const int piece = (lane & 15) ^ (tensor ? 2 * (r & 7) : (r & 15));
+      const int kpos = min(st * kPrefillKeys + r, nkeys - 1);
+      const size_t slot = (size_t)bt[kpos / BS] * BS + (kpos % BS);
+      src[j] = (tensor ? value_cache : key_cache) + slot * kv_dim + (size_t)h * D + piece * 8;
+      lds_base[j] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
+          buf + tensor * kPrefillKeys * kDirectRow + r0 * kDirectRow);
+    }
+    // global_load_lds_dwordx4 with the wave-uniform LDS base in M0. Written
+    // as inline asm so the compiler does not treat the loads as LDS writes
+    // that every later LDS read must wait for: the loads go to the buffer the
+    // current stage does not read, and the stage loop waits for them itself
+    // (s_waitcnt vmcnt(0), then a barrier) before that buffer is read. Loads
+    // unknown to the compiler only make its own vmcnt waits more
+    // conservative (vector loads complete in order).
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(lds_base[j]), "v"(src[j]) : "memory", "m0");
+  };
+
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as the
+  // builtin so the compiler's own wait placement sees it.
+  constexpr int kWaitVmcnt0 = 0x0F70;
+  if constexpr (kDirect) {
+    issue_stage(0, s_d0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (nstages > 1) load_stage(1);
+  } else {
+    load_stage(0);
+    if constexpr (NBUF == 2) {
+      store_stage(0);
+      __syncthreads();
+      if (nstages > 1) load_stage(1);
+    }
   }
   for (int st = 0; st < nstages; ++st) {
-    if constexpr (NBUF == 1) {
+    if constexpr (!kDirect && NBUF == 1) {
       __syncthreads();                // every wave is done with the previous stage
       store_stage(0);
       __syncthreads();
       if (st + 1 < nstages) load_stage(st + 1);
     }
-    const uint8_t* s_k = s_kbuf[NBUF == 2 ? (st & 1) : 0];
-    const uint8_t* s_vt = s_vtbuf[NBUF == 2 ? (st & 1) : 0];
+    const uint8_t* s_k;
+    const uint8_t* s_vt;
+    if constexpr (kDirect) {
+      uint8_t* cur = (st & 1) ? s_d1 : s_d0;
+      uint8_t* nxt = (st & 1) ? s_d0 : s_d1;
+      // The next stage's loads go to the other buffer (last read in stage
+      // st - 1, which every wave finished before the barrier that ended it)
+      // and fly during this stage's math.
+      if (st + 1 < nstages) issue_stage(st + 1, nxt);
+      s_k = cur;
+      s_vt = cur + kPrefillKeys * kDirectRow;
+    } else {
+      s_k = s_kbuf[NBUF == 2 ? (st & 1) : 0];
+      s_vt = s_vtbuf[NBUF == 2 ? (st & 1) : 0];
+    }
     if (wrow0 < qn) {                 // a wave past the chunk's end only helps staging
 #pragma unroll
     for (int kp = 0; kp < kPrefillKeys / 32; ++kp) {
@@ -291,9 +310,16 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         uint4 ka[NK], kb[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-          ka[i] = *reinterpret_cast<const uint4*>(s_k + (lk + col) * KROW + (32 * i + 8 * grp) * 2);
-          kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * KROW +
-                                                  (32 * i + 8 * grp) * 2);
+          if constexpr (kDirect) {
+            // rows lk + col and lk + 16 + col both swizzle by col
+            const int sw = 16 * ((4 * i + grp) ^ col);
+            ka[i] = *reinterpret_cast<const uint4*>(s_k + (lk + col) * kDirectRow + sw);
+            kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * kDirectRow + sw);
+          } else {
+            ka[i] = *reinterpret_cast<const uint4*>(s_k + (lk + col) * KROW + (32 * i + 8 * grp) * 2);
+            kb[i] = *reinterpret_cast<const uint4*>(s_k + (lk + 16 + col) * KROW +
+                                                    (32 * i + 8 * grp) * 2);
+          }
         }
         // Wave priority: the softmax (a chain of dependent VALU work) runs
         // at priority 1 and the MFMA blocks at 0, so on a SIMD the wave in
@@ -384,8 +410,21 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           const int d = 16 * c + col;
           const uint8_t* vrow = s_vt + d * VTROW;
           uint4 a;
-          if constexpr (kPaired) {
-            a = *reinterpret_cast<const uint4*>(vrow + 16 * ((kp * 4 + grp) ^ (c & 7)));
+          if constexpr (kDirect) {
+            // Two transposing reads: in each 16-lane group, lane 4k + q points
+            // at dims 16c + 4q .. + 3 of key row lk + 16 half + 4 grp + k, and
+            // lane L receives dim 16c + L of those 4 keys: A[dim][8 grp + e].
+            const int k4 = (lane & 15) >> 2, q = lane & 3;
+            const int rr = 4 * grp + k4;                   // row within the 16-key tile
+            const int off = 16 * ((2 * c + (q >> 1)) ^ (2 * (rr & 7))) + 8 * (q & 1);
+            typedef short s4_lds __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) s4_lds lds_s4;
+            const s4_lds t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4*)(s_vt + (lk + rr) * kDirectRow + off));
+            const s4_lds t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4*)(s_vt + (lk + 16 + rr) * kDirectRow + off));
+            const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
+            a = make_uint4(u0.x, u0.y, u1.x, u1.y);
           } else {
             const uint2 va = *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 4 * grp));
             const uint2 vb =
@@ -407,7 +446,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         step(std::false_type{});
     }
     }
-    if constexpr (NBUF == 2) {
+    if constexpr (kDirect) {
+      // Stage st + 1 has landed once this wave's loads are done and every
+      // wave has passed the barrier (unconditional: with nothing in flight
+      // the wait costs nothing, and the compiler sees every load complete).
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    } else if constexpr (NBUF == 2) {
       // The other buffer was last read in stage st - 1; every wave has
       // passed the barrier that ended it.
       if (st + 1 < nstages) store_stage((st + 1) & 1);
