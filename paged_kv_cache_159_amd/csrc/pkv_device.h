@@ -101,22 +101,29 @@ __device__ __forceinline__ float group_sum(float x) {
 // 2^x with the hardware instruction (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Group of sequence s: the largest g < num_groups with group_start[g] <= s
-// (group_start is nondecreasing from 0 to num_seqs, so that g has
-// group_start[g] <= s < group_start[g + 1], skipping empty groups). Called by
-// a whole wave with the same s: lane i loads group_start[i] of each 64-entry
-// chunk and the count of entries <= s comes from a ballot, so the lookup costs
-// one memory round trip per 64 groups instead of a chain of dependent loads.
-__device__ __forceinline__ int group_of(int s, const int32_t* __restrict__ group_start,
-                                        int num_groups) {
+// Shared blocks of sequence s's group: shared_blocks[g] for the largest
+// g < num_groups with group_start[g] <= s (group_start is nondecreasing from 0
+// to num_seqs, so that g has group_start[g] <= s < group_start[g + 1],
+// skipping empty groups). Called by a whole wave with the same s: lane i loads
+// entry i of each 64-entry chunk of both arrays at once, a ballot counts the
+// starts <= s (a prefix of the chunk), and the last such lane's shared_blocks
+// entry is read across lanes. One memory round trip per 64 groups, with no
+// load waiting on another.
+__device__ __forceinline__ int group_shared_blocks(int s, const int32_t* __restrict__ group_start,
+                                                   const int32_t* __restrict__ shared_blocks,
+                                                   int num_groups) {
   const int lane = threadIdx.x & 63;
-  int count = 0;
+  int sb = 0;
   for (int base = 0; base < num_groups; base += 64) {
     const int g = base + lane;
-    const bool le = g < num_groups && group_start[g] <= s;
-    count += __popcll(__ballot(le));
+    const bool in = g < num_groups;
+    const int gs = in ? group_start[g] : 0;
+    const int sbv = in ? shared_blocks[g] : 0;
+    const int c = __popcll(__ballot(in && gs <= s));   // wave-uniform
+    if (c > 0) sb = __builtin_amdgcn_readlane(sbv, c - 1);
+    if (c < 64) break;                                  // later starts are past s
   }
-  return count > 0 ? count - 1 : 0;   // group_start[0] = 0, so count >= 1
+  return sb;
 }
 
 }  // namespace pkv

@@ -13,7 +13,8 @@
 // row by row, so the MFMA shape is the same at every block size.
 //
 // One 8-wave workgroup per (group, chunk of kSharedChunkTiles shared tiles,
-// head); up to 16 queries per MFMA tile (larger groups loop over tiles).
+// group of heads); up to 16 queries per MFMA tile (larger groups loop over
+// tiles).
 //   S^T = K Q^T with v_mfma_f32_16x16x32 (M = 16 tokens, N = 16 queries,
 //   K = 32 dims per instruction), A operand (lane l: token l%16, 8 dims) read
 //   from the K rows staged in LDS, B operand (query l%16) from Q. Lane group
@@ -21,8 +22,8 @@
 //   The accumulator holds S^T[token 4*(l/16)+v][query l%16] (v < 4): exactly
 //   the B-operand layout P^T needs for O^T = V^T P^T with v_mfma_f32_16x16x16
 //   (K = 16 tokens), so P never moves between lanes.
-//   V^T's A operand wants 4 tokens of one dim per lane, a transposed read from
-//   the V rows staged in LDS (rows padded to spread banks).
+//   V^T's A operand wants 4 tokens of one dim per lane: one transposing LDS
+//   read (ds_read_b64_tr_b16) from the row-major V rows.
 //   P is split into hi + lo 16-bit parts (two MFMAs), so the 16-bit operand
 //   costs no accuracy next to the fp32 softmax.
 // The unit writes (max, sum, normalised output) partials for its chunk; the
@@ -39,32 +40,38 @@ namespace pkv {
 constexpr int kQueryTile = 16;
 constexpr int kGroupedWaves = 8;   // same workgroup shape as the partition kernel
 
-// Heads per shared-prefix unit: PKV_SHARED_ROW_BYTES / (2 D), so one token
-// row of the unit's heads is that many contiguous bytes of K (or V); a single
-// head's 256-byte slices at the pool's token stride stream far slower from
-// HBM. The waves split the heads, then each head's output dims.
-#ifndef PKV_SHARED_ROW_BYTES
-#define PKV_SHARED_ROW_BYTES 512
-#endif
+// Bytes of one token row of a shared-prefix unit's heads: the unit takes
+// kSharedRowBytes / (2 D) heads (2 at D = 128, 4 at D = 64), so one token row
+// of its heads is that many contiguous bytes of K (or V); a single head's
+// 256-byte slices at the pool's token stride stream far slower from HBM. The
+// waves split the heads, then each head's output dims.
+constexpr int kSharedRowBytes = 512;
 template <int D>
-constexpr int shared_heads() { return PKV_SHARED_ROW_BYTES / (2 * D); }
+constexpr int shared_heads() { return kSharedRowBytes / (2 * D); }
 
-// LDS bytes of one shared-prefix unit: K and V rows of its heads for one tile,
-// rows padded by 16 bytes to spread LDS banks.
-template <int D>
-constexpr int shared_row_bytes() { return 2 * D + 16; }
-template <int D>
-constexpr int shared_lds_bytes() { return 2 * shared_heads<D>() * kTileTokens * shared_row_bytes<D>(); }
+// LDS of one shared-prefix unit: a ring of kSharedBuffers tile buffers, each
+// the K rows then the V rows of the unit's heads for one 16-token tile
+// (unpadded 512-byte rows of XOR-swizzled 16-byte pieces).
+constexpr int kSharedBuffers = 3;
+constexpr int kSharedTileBytes = 2 * kTileTokens * kSharedRowBytes;
+constexpr int kSharedLdsBytes = kSharedBuffers * kSharedTileBytes;
 
 // One shared-prefix unit (group g, chunk of kSharedChunkTiles shared tiles,
 // head group hg of shared_heads<D>() heads) on an 8-wave workgroup over
-// blocks of BS tokens. The chunk's tiles stream through one LDS tile buffer:
-// each thread holds its four 16-byte pieces of the next tile in registers
-// while the waves compute on the current one (two barriers per tile). Wave w
-// takes head w / (8 / HU) of the group: S^T = K Q^T for that head (the few
-// MFMAs are repeated by the head's other wave) and 64 output dims of
-// O^T = V^T P^T. Groups larger than 16 run the chunk once per 16-query tile
-// (the re-reads hit L2).
+// blocks of BS tokens.
+// Staging: the tiles go from global memory straight into the LDS ring
+// (global_load_lds_dwordx4), two tiles ahead of the one being computed, so a
+// unit keeps 32 KiB in flight without staging registers. Wave w loads token
+// rows 2w and 2w + 1 of a tile, K and V one instruction each: lane l fills
+// slot l % 32 of row r = 2w + l / 32 with the row's piece slot ^ swizzle(r).
+// K swizzles by r & 15 (the 16 rows one S^T operand read touches land on
+// distinct banks), V by 2 (r & 7) (the transposing reads take 4 rows x 4
+// dims per 16 lanes). XOR on the low four bits keeps a piece in its half row.
+// Compute: wave w takes head w / (8 / HU) of the unit: S^T = K Q^T for that
+// head (the few MFMAs are repeated by the head's other waves) and NPV 16-dim
+// chunks of O^T = V^T P^T, whose A operand (4 tokens of one dim per lane) is
+// one transposing LDS read (ds_read_b64_tr_b16). Groups larger than 16 run
+// the chunk once per 16-query tile (the re-reads hit L2).
 template <typename T, int D, int BS>
 __device__ __forceinline__ void shared_unit(
     int g, int chunk, int hg, float* __restrict__ ws_ml, float* __restrict__ ws_o,
@@ -77,16 +84,13 @@ __device__ __forceinline__ void shared_unit(
   constexpr int HU = shared_heads<D>();
   constexpr int WPH = kGroupedWaves / HU;      // waves per head
   constexpr int NQK = D / 32;                  // S MFMAs (32 dims each)
-  constexpr int NPV = D / 16 / WPH;            // 16-dim output chunks per wave (4)
+  constexpr int NPV = D / 16 / WPH;            // 16-dim output chunks per wave
   constexpr int SPAN = D / 4;                  // dims per lane group in the S contraction
-  constexpr int ROW = shared_row_bytes<D>();
-  constexpr int THREADS = kGroupedWaves * 64;
-  constexpr int ROW_PIECES = HU * D / 8;       // 16-byte pieces of one token row of the heads
-  constexpr int TILE_PIECES = 2 * kTileTokens * ROW_PIECES;   // K and V of one tile
-  constexpr int PPT = TILE_PIECES / THREADS;   // pieces per thread per tile
-  constexpr int V_OFF = HU * kTileTokens * ROW;  // LDS byte offset of the V rows
-  static_assert(64 % ROW_PIECES == 0 && PPT * THREADS == TILE_PIECES,
-                "whole row segments per wave load");
+  constexpr int HP = D / 8;                    // 16-byte pieces of one head's row
+  constexpr int ROWB = kSharedRowBytes;
+  constexpr int V_OFF = kTileTokens * ROWB;    // V rows after the K rows of a tile buffer
+  static_assert(HU * HP == 32 && 2 * kGroupedWaves == kTileTokens,
+                "a wave's load instruction is two whole token rows of the unit");
   static_assert(WPH * HU == kGroupedWaves && NPV * 16 * WPH == D, "waves split heads and dims");
   const int st = shared_prefix_tokens(shared_blocks[g], BS);
   const int t0_chunk = chunk * kSharedChunkTiles * kTileTokens;
@@ -99,60 +103,60 @@ __device__ __forceinline__ void shared_unit(
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const uint32_t kv_dim = (uint32_t)H * D;
-  // The group's first member's table: the shared entries are the same in all.
-  const int32_t* bt = block_tables + (size_t)s0 * max_blocks;
+  const size_t kv_dim = (size_t)H * D;
   const int hw = wave / WPH;                   // this wave's head within the unit
   const int h = hg * HU + hw;
   const bool head_ok = h < H;                  // wave-uniform
   const int dim0 = (wave % WPH) * (NPV * 16);  // first output dim of this wave
 
-  // This thread's pieces of a tile: piece e = threadIdx.x % ROW_PIECES of the
-  // row segment (head e / (D / 8), column e % (D / 8)) in token rows
-  // r_j = threadIdx.x / ROW_PIECES + j * RSTEP, j < RPT, of both K and V.
-  // Token t of the prefix is at slot block_table[t / BS] * BS + t % BS, whose
-  // row starts at byte slot * kv_dim * 2; the unit's heads start at hg * HU * D.
-  constexpr int RPT = PPT / 2;                 // token rows per thread per tile
-  constexpr int RSTEP = THREADS / ROW_PIECES;  // rows covered by one pass of the threads
-  static_assert(RPT * RSTEP == kTileTokens, "the threads cover the tile's rows");
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 pk[RPT], pv[RPT];
-  const int e = threadIdx.x % ROW_PIECES;
-  const int r0 = threadIdx.x / ROW_PIECES;
-  const bool piece_ok = hg * HU + e / (D / 8) < H;
-  const char* kbase = reinterpret_cast<const char*>(key_cache + (size_t)hg * HU * D);
-  const char* vbase = reinterpret_cast<const char*>(value_cache + (size_t)hg * HU * D);
-  const size_t row_bytes = (size_t)kv_dim * sizeof(uint16_t);
-  auto load_tile = [&](int b) {
-    const int tb = t0_chunk + b * kTileTokens;   // a multiple of 16
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int t = tb + r0 + j * RSTEP;
-      // At block sizes >= 16 the whole tile is in the block of tb.
-      const int32_t phys = bt[(BS >= kTileTokens ? tb : t) / BS];
-      const size_t off = ((size_t)phys * BS + (t % BS)) * row_bytes + e * 16;
-      if (piece_ok) {
-        pk[j] = *reinterpret_cast<const u32x4*>(kbase + off);
-        pv[j] = *reinterpret_cast<const u32x4*>(vbase + off);
-      }
-    }
+  // The chunk's table entries (the group's first member's table: the shared
+  // entries are the same in all), one per lane, read with v_readlane. A chunk
+  // starts on a multiple of 128 tokens, so on a block boundary.
+  const int32_t* bt = block_tables + (size_t)s0 * max_blocks;
+  const int blk0 = t0_chunk / BS;
+  const int nblk = (nt * kTileTokens + BS - 1) / BS;   // <= 16
+  const int32_t table_lane = lane < nblk ? bt[blk0 + lane] : 0;
+  // This lane's load: row lrow of each tile, the pieces the K and V swizzles
+  // put in its slot. Pieces of heads past H (a partial last head group)
+  // re-read the unit's first head; nothing reads their slots.
+  const int lrow = 2 * wave + (lane >> 5);
+  auto piece_elems = [&](int p) {
+    return (uint32_t)(hg * HU * D + (hg * HU + p / HP < H ? p : p % HP) * 8);
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int at = ((e / (D / 8)) * kTileTokens + r0 + j * RSTEP) * ROW + (e % (D / 8)) * 16;
-      if (piece_ok) {
-        *reinterpret_cast<u32x4*>(lds + at) = pk[j];
-        *reinterpret_cast<u32x4*>(lds + V_OFF + at) = pv[j];
-      }
-    }
+  const uint32_t k_elem = piece_elems((lane & 31) ^ (lrow & 15));
+  const uint32_t v_elem = piece_elems((lane & 31) ^ (2 * (lrow & 7)));
+  auto lds_addr = [](const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p);
   };
-  const uint8_t* s_k = lds + hw * kTileTokens * ROW;
-  const uint8_t* s_v = lds + V_OFF + hw * kTileTokens * ROW;
+  // Tile b of the chunk into ring buffer buf. Rows 2w and 2w + 1 lie in one
+  // block (tiles start on multiples of 16 tokens, blocks hold 8 or more).
+  // The loads are inline asm so that the compiler does not treat them as LDS
+  // writes every later LDS read must wait for; the loop below waits for them
+  // itself (s_waitcnt vmcnt, then a barrier) before a buffer is read.
+  auto issue_tile = [&](int b, uint8_t* buf) {
+    const int tw = t0_chunk + b * kTileTokens + 2 * wave;   // wave-uniform
+    const int32_t phys = __builtin_amdgcn_readlane(table_lane, tw / BS - blk0);
+    const size_t row = ((size_t)phys * BS + (tw % BS) + (lane >> 5)) * kv_dim;
+    const uint16_t* ks = key_cache + row + k_elem;
+    const uint16_t* vs = value_cache + row + v_elem;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr(buf + 2 * wave * ROWB)), "v"(ks) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr(buf + V_OFF + 2 * wave * ROWB)), "v"(vs) : "memory", "m0");
+  };
+  // s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima.
+  constexpr int kWaitVmcnt0 = 0x0F70, kWaitVmcnt2 = 0x0F72;
+  // LDS reads of this lane: S^T operand i at row col, piece hw HP + grp SPAN / 8
+  // + i; V^T operand of chunk c: lane 4 k4 + q of its 16-lane group points at
+  // dims dim0 + 16 c + 4 q .. + 3 of row 4 grp + k4 and receives dim
+  // dim0 + 16 c + col of those 4 rows (tokens 4 grp .. 4 grp + 3).
+  const int k4 = (lane & 15) >> 2, q4 = lane & 3;
+  const int vr = 4 * grp + k4;
 
   for (int t0 = s0; t0 < s1; t0 += kQueryTile) {
     const int sq = t0 + col;
     const bool q_ok = sq < s1 && head_ok;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 qf[NQK];
 #pragma unroll
     for (int i = 0; i < NQK; ++i)
@@ -163,19 +167,27 @@ __device__ __forceinline__ void shared_unit(
 #pragma unroll
     for (int c = 0; c < NPV; ++c) acc[c] = f4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
-    load_tile(0);
+    issue_tile(0, lds);
+    if (nt > 1) issue_tile(1, lds + kSharedTileBytes);
     for (int b = 0; b < nt; ++b) {
-      // Every wave is done with the buffer's previous tile (and, at b = 0,
-      // with the previous query tile's last one).
+      // Tile b has landed once this wave's loads up to it are done (only tile
+      // b + 1's two may still fly: loads complete in order) and every wave
+      // has passed the barrier.
+      if (b + 1 < nt)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt2);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      store_tile();
-      __syncthreads();
-      if (b + 1 < nt) load_tile(b + 1);
+      // Tile b + 2 goes to the buffer tile b - 1 used; every wave finished
+      // reading it before the barrier.
+      if (b + 2 < nt) issue_tile(b + 2, lds + ((b + 2) % kSharedBuffers) * kSharedTileBytes);
+      const uint8_t* s_k = lds + (b % kSharedBuffers) * kSharedTileBytes;
+      const uint8_t* s_v = s_k + V_OFF;
       f4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
-        const uint4 kf =
-            *reinterpret_cast<const uint4*>(s_k + col * ROW + (grp * SPAN + 8 * i) * 2);
+        const int p = hw * HP + grp * (SPAN / 8) + i;
+        const uint4 kf = *reinterpret_cast<const uint4*>(s_k + col * ROWB + 16 * (p ^ col));
         sacc = M::k32(kf, __builtin_bit_cast(uint4, qf[i]), sacc);
       }
       // sacc[v] = S^T[token 4*grp + v][query col]; shared tiles are full.
@@ -205,12 +217,12 @@ __device__ __forceinline__ void shared_unit(
       const uint2 blo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
 #pragma unroll
       for (int c = 0; c < NPV; ++c) {
-        const uint8_t* vp = s_v + (4 * grp) * ROW + (dim0 + 16 * c + col) * 2;
-        const uint32_t a0 = *reinterpret_cast<const uint16_t*>(vp);
-        const uint32_t a1 = *reinterpret_cast<const uint16_t*>(vp + ROW);
-        const uint32_t a2 = *reinterpret_cast<const uint16_t*>(vp + 2 * ROW);
-        const uint32_t a3 = *reinterpret_cast<const uint16_t*>(vp + 3 * ROW);
-        const uint2 av = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+        const int p = hw * HP + (dim0 + 16 * c) / 8 + (q4 >> 1);
+        typedef short s4_lds __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s4_lds lds_s4;
+        const s4_lds t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4*)(s_v + vr * ROWB + 16 * (p ^ (2 * (vr & 7))) + 8 * (q4 & 1)));
+        const uint2 av = __builtin_bit_cast(uint2, t);
         acc[c] = M::k16(av, bhi, acc[c] * alpha);
         acc[c] = M::k16(av, blo, acc[c]);
       }
@@ -228,6 +240,8 @@ __device__ __forceinline__ void shared_unit(
         ws_ml[pi * 2 + 1] = l;
       }
     }
+    // The next query tile's first loads overwrite the ring.
+    __syncthreads();
   }
 }
 
@@ -252,8 +266,8 @@ decode_grouped_kernel(float* __restrict__ ws_ml, float* __restrict__ ws_o,
                       const int32_t* __restrict__ shared_blocks, int num_groups, int num_seqs,
                       int num_heads, int max_blocks, int num_parts, int chunk_slots,
                       int tail_wgs, float scale_log2, int32_t* __restrict__ seq_tok0) {
-  constexpr int kLds = shared_lds_bytes<D>() > partition_lds_bytes<D>() ? shared_lds_bytes<D>()
-                                                                         : partition_lds_bytes<D>();
+  constexpr int kLds = kSharedLdsBytes > partition_lds_bytes<D>() ? kSharedLdsBytes
+                                                                  : partition_lds_bytes<D>();
   __shared__ __align__(16) uint8_t lds[kLds];
   if ((int)blockIdx.x < tail_wgs) {
     partition_body<T, D, PT, BS, true>(blockIdx.x, nullptr, ws_ml, ws_o, query, key_cache,

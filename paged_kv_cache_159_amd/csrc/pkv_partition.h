@@ -59,7 +59,7 @@ __device__ __forceinline__ void partition_body(
   const int ctx = context_lens[s];
   int tok0 = 0;   // first token this launch covers for sequence s
   if constexpr (TAIL)
-    tok0 = shared_prefix_tokens(shared_blocks[group_of(s, group_start, num_groups)], BS);
+    tok0 = shared_prefix_tokens(group_shared_blocks(s, group_start, shared_blocks, num_groups), BS);
   if constexpr (TAIL) {
     if (p == 0 && g == 0 && threadIdx.x == 0) seq_tok0[s] = tok0;
   }
