@@ -338,106 +338,144 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         }
         constexpr bool kSplit = std::is_same<T, BF16>::value;
         uint4 bhi[QW], blo[QW];
-        float mnew[QW], psum[QW];
-        bool moved = false;
+        float psum[QW];
         __builtin_amdgcn_s_setprio(1);
+        // Exponents against the current reference: y = s * scale - m in the
+        // log2 domain, one FMA per score (masked keys -inf). The reference
+        // stays unless some score of the step exceeds it by more than
+        // kRefSlack, which each lane tests on its own 8 scores (no cross-lane
+        // max in the common case). Every weight is then at most 2^kRefSlack,
+        // well inside the 16-bit range; softmax does not depend on the
+        // reference.
+        float y[QW][8];
+        bool over = false;
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
-          // Scaled scores in the log2 domain (products are canonical floats,
-          // so the max below needs no quieting of its inputs).
-          float x[8];
+          const float nm = -m[j];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            x[v] = sa[j][v] * scale_log2;
-            x[4 + v] = sb[j][v] * scale_log2;
+            y[j][v] = __builtin_fmaf(sa[j][v], scale_log2, nm);
+            y[j][4 + v] = __builtin_fmaf(sb[j][v], scale_log2, nm);
           }
           if constexpr (kMask) {
             const int qpos = first + wrow0 + 16 * j + col;   // this lane's query position
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              if (kbase + 4 * grp + v > qpos) x[v] = -INFINITY;
-              if (kbase + 16 + 4 * grp + v > qpos) x[4 + v] = -INFINITY;
+              if (kbase + 4 * grp + v > qpos) y[j][v] = -INFINITY;
+              if (kbase + 16 + 4 * grp + v > qpos) y[j][4 + v] = -INFINITY;
             }
           }
-          float bm = x[0];
+          float lm = y[j][0];
 #pragma unroll
-          for (int e = 1; e < 8; ++e) bm = fmaxf(bm, x[e]);
-          bm = lane_group4_max(bm);
-          // Reference for the weights: raised to the step's max only when
-          // that exceeds it by more than kRefSlack (log2 units), so every
-          // weight stays at most 2^kRefSlack, well inside the 16-bit range.
-          // Softmax does not depend on the reference, and most steps keep
-          // it, which skips the rescale of the accumulators below. The first
-          // step holds key 0, which every query sees, so the reference is
-          // finite from then on; a step whose keys are all masked for a
-          // query keeps it.
-          mnew[j] = (bm > m[j] + kRefSlack) ? bm : m[j];
-          moved |= mnew[j] != m[j];
-          const float nm = -mnew[j];
-          float p[8], ps = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[e] + nm);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ps += p[e];
-          psum[j] = lane_group4_sum(ps);
-          uint32_t hi[4], lo[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hi[e] = E::pack2(p[2 * e], p[2 * e + 1]);
-            if constexpr (kSplit)
-              lo[e] = E::pack2(p[2 * e] - M::widen(hi[e] & 0xffffu), p[2 * e + 1] - M::widen(hi[e] >> 16));
-          }
-          bhi[j] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-          blo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          for (int e = 1; e < 8; ++e) lm = fmaxf(lm, y[j][e]);
+          over |= lm > kRefSlack;
         }
-        if (__builtin_expect(__any(moved), 0)) {         // wave-uniform, rare
+        // Weights, their row sums and the 16-bit P operands from y.
+        auto weights = [&]() {
 #pragma unroll
           for (int j = 0; j < QW; ++j) {
-            const float alpha = fast_exp2(m[j] - mnew[j]);  // exactly 1 where kept
+            float p[8], ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(y[j][e]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ps += p[e];
+            psum[j] = lane_group4_sum(ps);
+            uint32_t hi[4], lo[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hi[e] = E::pack2(p[2 * e], p[2 * e + 1]);
+              if constexpr (kSplit)
+                lo[e] = E::pack2(p[2 * e] - M::widen(hi[e] & 0xffffu), p[2 * e + 1] - M::widen(hi[e] >> 16));
+            }
+            bhi[j] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            blo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          }
+        };
+        // O^T += V^T P^T. Written once and placed on both sides of the rare
+        // rescale below, so that each side ends in the MFMAs that update the
+        // accumulators in place (a rescale joining a shared P.V block made
+        // the compiler copy all 64 accumulator registers every step).
+        auto pv_block = [&]() {
+          __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int d = 16 * c + col;
+            const uint8_t* vrow = s_vt + d * VTROW;
+            uint4 a;
+            if constexpr (kDirect) {
+              // Two transposing reads: in each 16-lane group, lane 4k + q points
+              // at dims 16c + 4q .. + 3 of key row lk + 16 half + 4 grp + k, and
+              // lane L receives dim 16c + L of those 4 keys: A[dim][8 grp + e].
+              const int k4 = (lane & 15) >> 2, q = lane & 3;
+              const int rr = 4 * grp + k4;                   // row within the 16-key tile
+              const int off = 16 * ((2 * c + (q >> 1)) ^ (2 * (rr & 7))) + 8 * (q & 1);
+              typedef short s4_lds __attribute__((ext_vector_type(4)));
+              typedef __attribute__((address_space(3))) s4_lds lds_s4;
+              const s4_lds t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s4*)(s_vt + (lk + rr) * kDirectRow + off));
+              const s4_lds t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s4*)(s_vt + (lk + 16 + rr) * kDirectRow + off));
+              const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
+              a = make_uint4(u0.x, u0.y, u1.x, u1.y);
+            } else {
+              const uint2 va = *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 4 * grp));
+              const uint2 vb =
+                  *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 16 + 4 * grp));
+              a = make_uint4(va.x, va.y, vb.x, vb.y);
+            }
+#pragma unroll
+            for (int j = 0; j < QW; ++j) {
+              f4_t t = M::k32(a, bhi[j], acc[j][c]);
+              if constexpr (kSplit) t = M::k32(a, blo[j], t);
+              acc[j][c] = t;
+            }
+          }
+        };
+        if (__builtin_expect(__any(over), 0)) {          // wave-uniform, rare
+          // Some score exceeds the reference by more than the slack (or this
+          // is the first step, whose reference is -inf): raise the reference
+          // of each query whose step max exceeds it by more than kRefSlack to
+          // that max, rescale its sums and accumulators, recompute y. The
+          // first step holds key 0, which every query sees, so the reference
+          // is finite from then on; a step whose keys are all masked for a
+          // query keeps it.
+#pragma unroll
+          for (int j = 0; j < QW; ++j) {
+            float x[8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              x[v] = sa[j][v] * scale_log2;
+              x[4 + v] = sb[j][v] * scale_log2;
+            }
+            if constexpr (kMask) {
+              const int qpos = first + wrow0 + 16 * j + col;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                if (kbase + 4 * grp + v > qpos) x[v] = -INFINITY;
+                if (kbase + 16 + 4 * grp + v > qpos) x[4 + v] = -INFINITY;
+              }
+            }
+            float bm = x[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) bm = fmaxf(bm, x[e]);
+            bm = lane_group4_max(bm);
+            const float mnew = (bm > m[j] + kRefSlack) ? bm : m[j];
+            const float alpha = fast_exp2(m[j] - mnew);    // exactly 1 where kept
             l[j] *= alpha;
 #pragma unroll
             for (int c = 0; c < NC; ++c) acc[j][c] *= alpha;
+            m[j] = mnew;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[j][e] = x[e] - mnew;
           }
+          weights();
+          pv_block();
+        } else {
+          weights();
+          pv_block();
         }
 #pragma unroll
-        for (int j = 0; j < QW; ++j) {
-          l[j] += psum[j];
-          m[j] = mnew[j];
-        }
-        __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int d = 16 * c + col;
-          const uint8_t* vrow = s_vt + d * VTROW;
-          uint4 a;
-          if constexpr (kDirect) {
-            // Two transposing reads: in each 16-lane group, lane 4k + q points
-            // at dims 16c + 4q .. + 3 of key row lk + 16 half + 4 grp + k, and
-            // lane L receives dim 16c + L of those 4 keys: A[dim][8 grp + e].
-            const int k4 = (lane & 15) >> 2, q = lane & 3;
-            const int rr = 4 * grp + k4;                   // row within the 16-key tile
-            const int off = 16 * ((2 * c + (q >> 1)) ^ (2 * (rr & 7))) + 8 * (q & 1);
-            typedef short s4_lds __attribute__((ext_vector_type(4)));
-            typedef __attribute__((address_space(3))) s4_lds lds_s4;
-            const s4_lds t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s4*)(s_vt + (lk + rr) * kDirectRow + off));
-            const s4_lds t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s4*)(s_vt + (lk + 16 + rr) * kDirectRow + off));
-            const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
-            a = make_uint4(u0.x, u0.y, u1.x, u1.y);
-          } else {
-            const uint2 va = *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 4 * grp));
-            const uint2 vb =
-                *reinterpret_cast<const uint2*>(vrow + vt_key_offset(d, lk + 16 + 4 * grp));
-            a = make_uint4(va.x, va.y, vb.x, vb.y);
-          }
-#pragma unroll
-          for (int j = 0; j < QW; ++j) {
-            f4_t t = M::k32(a, bhi[j], acc[j][c]);
-            if constexpr (kSplit) t = M::k32(a, blo[j], t);
-            acc[j][c] = t;
-          }
-        }
+        for (int j = 0; j < QW; ++j) l[j] += psum[j];
         __builtin_amdgcn_s_setprio(1);
       };
       if (kbase + 31 > first + wrow0)
