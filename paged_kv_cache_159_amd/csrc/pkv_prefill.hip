@@ -16,32 +16,37 @@
 // rows, head); each wave owns 32 query rows as two 16-column MFMA tiles. Tiles
 // are dispatched last-first (the causal work of a tile grows with its
 // position). Keys are staged through LDS 64 at a time, gathered row by row
-// through the block table (any block size), into two LDS buffers: the next
-// stage's rows arrive while the waves compute on the current one (one barrier
-// per stage). At head size 128 the rows go from global memory straight into
-// LDS (global_load_lds_dwordx4), K and V both row-major with XOR-swizzled
-// 16-byte pieces, and P.V reads its V^T operands with gfx950's transposing
-// LDS read (ds_read_b64_tr_b16). Other head sizes stage through registers:
-// K rows padded by 16 bytes, V transposed into V^T[dim][key] element by
-// element.
+// through the block table (any block size); one barrier per stage. At head
+// size 128 the rows go from global memory straight into a ring of three LDS
+// buffers (global_load_lds_dwordx4; the next two stages arrive while the
+// waves compute on the current one), K and V both row-major with
+// XOR-swizzled 16-byte pieces, and P.V reads its V^T operands with gfx950's
+// transposing LDS read (ds_read_b64_tr_b16). Other head sizes stage through
+// registers into two buffers: K rows padded by 16 bytes, V transposed into
+// V^T[dim][key] element by element.
 //
 // Arithmetic, per 32 keys and 16 queries:
 //   S^T = K Q^T with v_mfma_f32_16x16x32 (A = 16 key rows, B = the queries'
 //   rows), two 16-key tiles; the accumulator holds S^T[key 4g+v][query l%16].
 //   Causal mask (key position > query position -> -inf; only on steps that
 //   reach past the wave's first query), online softmax per query column in
-//   the log2 domain (max and sum across the 4 lane groups by gfx950's
-//   row-swap instructions), against a reference that moves only when a score
-//   exceeds it by more than 2^8, so most steps skip the rescale.
+//   the log2 domain against a reference that moves only when a score
+//   exceeds it by more than 8 (log2 units): the exponent of a score is one
+//   FMA, and each lane tests its own scores against the slack; only a step
+//   that moves the reference takes the max across the 4 lane groups
+//   (gfx950's row-swap instructions) and rescales.
 //   O^T += V^T P^T with one v_mfma_f32_16x16x32 per 16 output dims: its K index
 //   8g+e runs over keys 4g+e of the first tile (e < 4) and 16+4g+(e-4) of the
 //   second, which is exactly where the two S^T accumulators already hold P^T,
 //   so P never moves between lanes; V^T's operand is two 8-byte LDS reads
 //   (transposing reads of the row-major V at head size 128).
-//   fp16: P is rounded once to fp16 (11-bit significand; the sum l stays
-//   fp32). bf16: rounding P to bf16's 8 bits made ~0.1% of outputs miss half
-//   an output ulp against the exact result, so P is split into hi + lo bf16
-//   parts and V^T P^T takes two MFMAs per 16 dims.
+//   The row sums of the weights come from one more MFMA per tile: the same P
+//   operand against all-ones rows (so the denominator sums exactly the
+//   weights the numerator used).
+//   fp16: P is rounded once to fp16 (11-bit significand). bf16: rounding P to
+//   bf16's 8 bits made ~0.1% of outputs miss half an output ulp against the
+//   exact result, so P is split into hi + lo bf16 parts and V^T P^T takes
+//   two MFMAs per 16 dims.
 
 #include <type_traits>
 
@@ -125,11 +130,12 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   constexpr bool kDirect = D == 128 && kPrefillKeys == 64 && kPrefillWaves == 8;
   constexpr int kDirectRow = 2 * D;                       // 256 bytes
   constexpr int kDirectStage = 2 * kPrefillKeys * kDirectRow;   // K rows, then V rows
-  // Two separate arrays (not one indexed by the stage's parity), so the
-  // compiler can tell that the reads of one stage do not alias the loads in
-  // flight into the other and need not wait for them.
+  // A ring of three stage buffers: the loads of stages st + 1 and st + 2 fly
+  // while stage st is computed (the kernel's registers allow one workgroup
+  // per CU, so its LDS can take 96 KiB).
   __shared__ __align__(16) uint8_t s_d0[kDirect ? kDirectStage : 16];
   __shared__ __align__(16) uint8_t s_d1[kDirect ? kDirectStage : 16];
+  __shared__ __align__(16) uint8_t s_d2[kDirect ? kDirectStage : 16];
   __shared__ __align__(16) uint8_t s_kbuf[kDirect ? 1 : NBUF][kDirect ? 16 : kPrefillKeys * KROW];
   constexpr int VTROW = kVtRow;
   __shared__ __align__(16) uint8_t s_vtbuf[kDirect ? 1 : NBUF][kDirect ? 16 : D * VTROW];
@@ -163,11 +169,15 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
                           : make_uint4(0, 0, 0, 0);
   }
   f4_t acc[QW][NC];
-  float m[QW], l[QW];
+  // m: softmax reference per query row (log2 domain); lsum: the row sums of
+  // the weights, accumulated by an MFMA against an all-ones operand (every
+  // element of lsum[j] holds lane's query row sum).
+  float m[QW];
+  f4_t lsum[QW];
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     m[j] = -INFINITY;
-    l[j] = 0.f;
+    lsum[j] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[j][c] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -238,7 +248,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       const int r = r0 + (lane >> 4);
       const int piece = (lane & 15) ^ (tensor ? 2 * (r & 7) : (r & 15));
       const int kpos = min(st * kPrefillKeys + r, nkeys - 1);
-      const size_t slot = (size_t)bt[kpos / BS] * BS + (kpos % BS);
+      // The instruction's 4 rows (clamped or not) lie in one block, so its
+      // table entry is a scalar load (not a vector load, whose wait would
+      // also wait for the stage loads in flight).
+      const int32_t phys = bt[min(st * kPrefillKeys + r0, nkeys - 1) / BS];
+      const size_t slot = (size_t)phys * BS + (kpos % BS);
       src[j] = (tensor ? value_cache : key_cache) + slot * kv_dim + (size_t)h * D + piece * 8;
       lds_base[j] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
           buf + tensor * kPrefillKeys * kDirectRow + r0 * kDirectRow);
@@ -259,9 +273,15 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as the
   // builtin so the compiler's own wait placement sees it.
   constexpr int kWaitVmcnt0 = 0x0F70;
+  // s_waitcnt vmcnt(4): all but one stage's four loads of this wave done.
+  constexpr int kWaitVmcnt4 = 0x0F74;
   if constexpr (kDirect) {
+    // Stage 0 and the query rows first (waited for here, so the compiler
+    // knows the query registers are ready and puts no wait of its own in
+    // the loop, where it would also wait for the stages in flight).
     issue_stage(0, s_d0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (nstages > 1) issue_stage(1, s_d1);
     __syncthreads();
   } else {
     load_stage(0);
@@ -281,12 +301,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint8_t* s_k;
     const uint8_t* s_vt;
     if constexpr (kDirect) {
-      uint8_t* cur = (st & 1) ? s_d1 : s_d0;
-      uint8_t* nxt = (st & 1) ? s_d0 : s_d1;
-      // The next stage's loads go to the other buffer (last read in stage
-      // st - 1, which every wave finished before the barrier that ended it)
-      // and fly during this stage's math.
-      if (st + 1 < nstages) issue_stage(st + 1, nxt);
+      const int b = st % 3;
+      uint8_t* cur = b == 0 ? s_d0 : (b == 1 ? s_d1 : s_d2);
+      uint8_t* nxt2 = b == 0 ? s_d2 : (b == 1 ? s_d0 : s_d1);
+      // Stage st + 2's loads go to the buffer stage st - 1 used (every wave
+      // finished reading it before the barrier that ended stage st - 1) and
+      // fly during this stage's and the next one's math.
+      if (st + 2 < nstages) issue_stage(st + 2, nxt2);
       s_k = cur;
       s_vt = cur + kPrefillKeys * kDirectRow;
     } else {
@@ -338,7 +359,6 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         }
         constexpr bool kSplit = std::is_same<T, BF16>::value;
         uint4 bhi[QW], blo[QW];
-        float psum[QW];
         __builtin_amdgcn_s_setprio(1);
         // Exponents against the current reference: y = s * scale - m in the
         // log2 domain, one FMA per score (masked keys -inf). The reference
@@ -370,16 +390,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           for (int e = 1; e < 8; ++e) lm = fmaxf(lm, y[j][e]);
           over |= lm > kRefSlack;
         }
-        // Weights, their row sums and the 16-bit P operands from y.
+        // Weights and the 16-bit P operands from y.
         auto weights = [&]() {
 #pragma unroll
           for (int j = 0; j < QW; ++j) {
-            float p[8], ps = 0.f;
+            float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = fast_exp2(y[j][e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ps += p[e];
-            psum[j] = lane_group4_sum(ps);
             uint32_t hi[4], lo[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -430,6 +447,15 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
               acc[j][c] = t;
             }
           }
+          // Row sums: the same P operands against all-ones rows.
+          constexpr uint32_t kOne2 = std::is_same<T, BF16>::value ? 0x3F803F80u : 0x3C003C00u;
+          const uint4 ones = make_uint4(kOne2, kOne2, kOne2, kOne2);
+#pragma unroll
+          for (int j = 0; j < QW; ++j) {
+            f4_t t = M::k32(ones, bhi[j], lsum[j]);
+            if constexpr (kSplit) t = M::k32(ones, blo[j], t);
+            lsum[j] = t;
+          }
         };
         if (__builtin_expect(__any(over), 0)) {          // wave-uniform, rare
           // Some score exceeds the reference by more than the slack (or this
@@ -461,7 +487,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
             bm = lane_group4_max(bm);
             const float mnew = (bm > m[j] + kRefSlack) ? bm : m[j];
             const float alpha = fast_exp2(m[j] - mnew);    // exactly 1 where kept
-            l[j] *= alpha;
+            lsum[j] *= alpha;
 #pragma unroll
             for (int c = 0; c < NC; ++c) acc[j][c] *= alpha;
             m[j] = mnew;
@@ -474,8 +500,6 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           weights();
           pv_block();
         }
-#pragma unroll
-        for (int j = 0; j < QW; ++j) l[j] += psum[j];
         __builtin_amdgcn_s_setprio(1);
       };
       if (kbase + 31 > first + wrow0)
@@ -485,10 +509,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     }
     }
     if constexpr (kDirect) {
-      // Stage st + 1 has landed once this wave's loads are done and every
-      // wave has passed the barrier (unconditional: with nothing in flight
-      // the wait costs nothing, and the compiler sees every load complete).
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      // Stage st + 1 has landed once this wave's loads up to it are done
+      // (only stage st + 2's four may still fly: loads complete in order) and
+      // every wave has passed the barrier.
+      if (st + 2 < nstages)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
     } else if constexpr (NBUF == 2) {
       // The other buffer was last read in stage st - 1; every wave has
@@ -504,7 +531,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   for (int j = 0; j < QW; ++j) {
     const int row = wrow0 + 16 * j + col;
     if (row >= qn) continue;
-    const float inv = 1.f / l[j];
+    const float inv = 1.f / lsum[j][0];
     uint16_t* o = out + ((size_t)(q0 + row) * H + h) * D + 4 * grp;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
