@@ -52,6 +52,15 @@
  * slots are < num_blocks*block_size and unique within a call; copy pairs have
  * unique destinations that are not sources in the same call; for the grouped
  * call, the group constraints stated at paged_attention_decode_grouped.
+ *
+ * Debug checks: with the environment variable PAGED_KV_DEBUG set to "1" (read
+ * at every call), the decode, grouped decode, prefill, cache-write,
+ * block-copy and swap_blocks calls first check those preconditions with
+ * device kernels on `stream`, wait for them (so the call synchronises), and
+ * return PKV_ERR_DATA without launching anything else if one fails. The
+ * checks read only within the arrays' stated sizes. paged_attention_decode_merge
+ * is not checked; swap_blocks_dma and swap_blocks_staged check their host
+ * mappings always.
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H
@@ -73,8 +82,10 @@ typedef enum {
   PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
   PKV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
   PKV_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
-  PKV_ERR_MEMORY = -7       /* swap_blocks: a buffer is not device memory of the current
+  PKV_ERR_MEMORY = -7,      /* swap_blocks: a buffer is not device memory of the current
                                device or pinned host memory, or is smaller than its sizes */
+  PKV_ERR_DATA = -8         /* PAGED_KV_DEBUG=1 only: a data-dependent precondition does not
+                               hold; nothing was launched */
 } pkv_status;
 
 /* Library version, major*10000 + minor*100 + patch. */

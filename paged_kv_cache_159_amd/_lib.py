@@ -33,7 +33,8 @@ EXPORTS = (
 
 PKV_F16, PKV_BF16 = 0, 1
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_UNSUPPORTED",
-          -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_LAUNCH", -6: "PKV_ERR_ALIGN", -7: "PKV_ERR_MEMORY"}
+          -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_LAUNCH", -6: "PKV_ERR_ALIGN", -7: "PKV_ERR_MEMORY",
+          -8: "PKV_ERR_DATA"}
 
 _lib = None
 

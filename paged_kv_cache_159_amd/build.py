@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libpaged_kv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_grouped.hip", "pkv_prefill.hip", "pkv_cache.hip"]
+SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_grouped.hip", "pkv_prefill.hip", "pkv_cache.hip",
+           "pkv_debug.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -11,6 +11,7 @@
 
 #include "paged_kv.h"
 #include "pkv_device.h"
+#include "pkv_debug.h"
 #include "pkv_launch.h"
 
 namespace {
@@ -57,6 +58,28 @@ int check_workspace(void* ws, size_t bytes, size_t need) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+// With PAGED_KV_DEBUG=1: run `checks` (device checks of the call's
+// data-dependent preconditions) on the stream, wait for them, and return
+// PKV_ERR_DATA if one failed, before the call launches anything else.
+// Otherwise nothing is launched and PKV_OK is returned.
+template <typename F>
+int debug_gate(hipStream_t st, F&& checks) {
+  if (!pkv::debug_enabled()) return PKV_OK;
+  hipError_t e = pkv::debug_reset(st);
+  if (e == hipSuccess) e = checks();
+  unsigned status = 0u;
+  if (e == hipSuccess) e = pkv::debug_status(st, &status);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  return status ? PKV_ERR_DATA : PKV_OK;
+}
+
+int debug_decode(const pkv::DecodeArgs& a, int num_blocks, hipStream_t st) {
+  return debug_gate(st, [&] {
+    return pkv::debug_check_tables(a.block_tables, a.context_lens, a.num_seqs,
+                                   a.max_blocks_per_seq, a.block_size, num_blocks, 1, st);
+  });
+}
 
 int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void* key_cache,
                    const void* value_cache, const int32_t* block_tables,
@@ -183,6 +206,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PKV_ERR_DATA:
+      return "a data-dependent precondition does not hold (found by the PAGED_KV_DEBUG=1 "
+             "device checks; nothing was launched)";
     default: return "unknown status";
   }
 }
@@ -208,6 +234,7 @@ int paged_attention_decode_partitions(void* out, const void* query, const void* 
                           num_seqs, num_heads, head_dim, num_blocks, block_size,
                           max_blocks_per_seq, scale, dtype, workspace, workspace_bytes);
   if (rc || num_seqs == 0) return rc;
+  if ((rc = debug_decode(a, num_blocks, static_cast<hipStream_t>(stream)))) return rc;
   return status_of(pkv::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -254,6 +281,7 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
                           max_blocks_per_seq, scale, dtype, workspace, workspace_bytes);
   if (rc || num_seqs == 0) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = debug_decode(a, num_blocks, st))) return rc;
   rc = status_of(pkv::launch_decode_partitions(a, st));
   if (rc || a.num_parts <= 1) return rc;
   return status_of(pkv::launch_decode_merge(a, st));
@@ -321,6 +349,14 @@ int paged_attention_decode_grouped(void* out, const void* query, const void* key
       static_cast<char*>(workspace) +
       pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, a.num_parts));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = debug_gate(st, [&] {
+    hipError_t e = pkv::debug_check_tables(block_tables, context_lens, num_seqs,
+                                           max_blocks_per_seq, block_size, num_blocks, 1, st);
+    if (e != hipSuccess) return e;
+    return pkv::debug_check_groups(group_start, shared_blocks, num_groups, num_seqs, block_tables,
+                                   context_lens, max_blocks_per_seq, block_size, st);
+  });
+  if (rc) return rc;
   rc = status_of(pkv::launch_decode_grouped(a, st));
   if (rc) return rc;
   return status_of(pkv::launch_decode_merge(a, st));
@@ -337,9 +373,13 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
   if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
       (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
     return PKV_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = debug_gate(st, [&] {
+    return pkv::debug_check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size, st);
+  });
+  if (rc) return rc;
   return status_of(pkv::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
-                                                 num_tokens, num_heads * head_dim,
-                                                 static_cast<hipStream_t>(stream)));
+                                                 num_tokens, num_heads * head_dim, st));
 }
 
 int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping, int num_pairs,
@@ -355,9 +395,13 @@ int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping
   if (!key_cache || !value_cache || !block_mapping) return PKV_ERR_NULL;
   if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(block_mapping))
     return PKV_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = debug_gate(st, [&] {
+    return pkv::debug_check_pairs(block_mapping, num_pairs, num_blocks, num_blocks, true, st);
+  });
+  if (rc) return rc;
   return status_of(pkv::launch_copy_blocks(key_cache, value_cache, key_cache, value_cache,
-                                           block_mapping, num_pairs, block_elems, false,
-                                           static_cast<hipStream_t>(stream)));
+                                           block_mapping, num_pairs, block_elems, false, st));
 }
 
 int paged_attention_prefill(void* out, const void* query, const void* key_cache,
@@ -399,7 +443,15 @@ int paged_attention_prefill(void* out, const void* query, const void* key_cache,
   a.max_query_len = max_query_len;
   a.scale = scale;
   a.dtype = dtype;
-  return status_of(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = debug_gate(st, [&] {
+    hipError_t e = pkv::debug_check_tables(block_tables, context_lens, num_seqs,
+                                           max_blocks_per_seq, block_size, num_blocks, 0, st);
+    if (e != hipSuccess) return e;
+    return pkv::debug_check_prefill(query_start, context_lens, num_seqs, max_query_len, st);
+  });
+  if (rc) return rc;
+  return status_of(pkv::launch_prefill(a, st));
 }
 
 int swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
@@ -426,11 +478,17 @@ int swap_blocks(const void* src_key, const void* src_value, void* dst_key, void*
       (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv, &host_dst)) ||
       (rc = device_accessible(block_mapping, (size_t)num_pairs * 2 * sizeof(int32_t), &bm)))
     return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = debug_gate(st, [&] {
+    return pkv::debug_check_pairs(static_cast<const int32_t*>(bm), num_pairs, src_num_blocks,
+                                  dst_num_blocks, false, st);
+  });
+  if (rc) return rc;
   // The system-scope release (an L2 write-back in every workgroup) is needed
   // only when the kernel writes pinned host memory.
   return status_of(pkv::launch_copy_blocks(sk, sv, const_cast<void*>(dk), const_cast<void*>(dv),
                                            static_cast<const int32_t*>(bm), num_pairs,
-                                           block_elems, host_dst, static_cast<hipStream_t>(stream)));
+                                           block_elems, host_dst, st));
 }
 
 

@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_kv.h")
 
-OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALIGN, MEMORY = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALIGN, MEMORY, DATA = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x10000        # fake, 16-byte aligned "device" pointer (never dereferenced)
 MIS = 0x10008      # misaligned
 
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert L.pkv_version() >= 100
-    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALIGN, MEMORY):
+    for code in (OK, NULL, SHAPE, UNSUP, WS, LAUNCH, ALIGN, MEMORY, DATA):
         s = L.pkv_status_string(code).decode()
         assert s and s != "unknown status"
     assert L.pkv_status_string(42).decode() == "unknown status"
