@@ -408,6 +408,15 @@ def test_block_size_grouped_shared_prefix(bs):
 
 
 @pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_grouped_head_dim_64(bs):
+    """Head size 64 (four heads per shared-prefix unit, six heads: the last
+    unit half empty) over 8- and 32-token blocks, prefix of 100 tokens (a
+    partial last block copied on write), groups of 5."""
+    from workloads import make_shared_case
+    check_grouped(make_shared_case(3, 5, 100, 1, 40, 6, 64, "f16", seed=40 + bs, block_size=bs))
+
+
+@pytest.mark.parametrize("bs", [8, 32])
 def test_block_size_grouped_singleton_groups(bs):
     """One sequence per group sharing all its full blocks but the last: odd
     shared-block counts at block size 8 leave half a tile to the tail."""
