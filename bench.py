@@ -500,6 +500,37 @@ def load_traffic(key):
     return t.get("bytes_per_launch")
 
 
+def hbm_context(nbytes=1 << 30, reps=10):
+    """Measured HBM rates on this machine, as context for the 8 TB/s peak: a
+    device-to-device copy of a 1 GiB buffer (bytes read + written per second)
+    and a read-only pass over it (torch's fp32 sum). Medians of HIP events;
+    nothing here is part of the timed decode."""
+    import torch
+    src = torch.randn(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    def med(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([x.elapsed_time(y) for x, y in ts])) * 1e-3
+    t_copy = med(lambda: dst.copy_(src))
+    t_read = med(lambda: src.sum())
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * nbytes / t_copy / 1e9, 1),
+            "read_gbs": round(nbytes / t_read / 1e9, 1),
+            "what": "1 GiB device copy (read + write bytes) and read-only sum, median of "
+                    f"{reps} HIP-event timings; context for the 8 TB/s peak, not the denominator"}
+
+
 def cpu_baseline(w, budget_s):
     """The float64 oracle (as it is) on whole sequences of the same workload,
     one thread, until about budget_s seconds of CPU work; scaled to K+V GB/s."""
@@ -690,6 +721,7 @@ def main():
     }
     del kcs, vcs
     torch.cuda.empty_cache()
+    res["hbm_measured"] = hbm_context()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
