@@ -568,6 +568,61 @@ def cpu_baseline(w, budget_s):
             "seqs_per_s": round(done_seqs / el, 4)}
 
 
+# Workload and host-side cache state for the forked oracle workers (set by
+# cpu_baseline_pool just before the fork; the children read it, never the GPU).
+_CPU_STATE = None
+
+
+def _cpu_pool_worker(wid):
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    w, K, V, workers, budget_s = _CPU_STATE
+    tokens = seqs = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s:
+            for s in range(wid, w.num_seqs, workers):
+                pairs = [(s, h) for h in range(w.num_heads)]
+                oracle.paged_attention_decode(w.query, K, V, w.block_tables, w.context_lens,
+                                              w.scale, w.block_size, w.dtype, pairs=pairs)
+                tokens += int(w.context_lens[s])
+                seqs += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+    return tokens, seqs
+
+
+def cpu_baseline_pool(w, budget_s):
+    """The same float64 oracle on all host cores (at most 16 worker processes,
+    one thread each, sequences dealt round-robin), for about budget_s seconds.
+    Must run before this process touches the GPU: the workers are forked and
+    never hold a GPU handle."""
+    import multiprocessing as mp
+
+    import oracle
+    global _CPU_STATE
+    K, V = w.key_cache, w.value_cache
+    if len(w.copy_pairs):
+        K, V = oracle.copy_blocks(K, V, w.copy_pairs)
+    K, V = oracle.reshape_and_cache(w.new_key, w.new_value, K, V, w.slot_mapping, w.block_size)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    _CPU_STATE = (w, K, V, workers, budget_s)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        parts = pool.map(_cpu_pool_worker, range(workers))
+    el = time.perf_counter() - t0
+    _CPU_STATE = None
+    tokens = sum(p[0] for p in parts)
+    seqs = sum(p[1] for p in parts)
+    gbs = tokens * w.kv_bytes_per_token / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 numpy oracle, {workers} processes x 1 thread (sequences dealt "
+                      f"round-robin): {seqs} sequence decodes (all {w.num_heads} heads each, "
+                      f"{tokens} tokens) in {el:.1f} s wall, pool start included",
+            "seqs_per_s": round(seqs / el, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -590,9 +645,23 @@ def main():
         traffic_summary(args.traffic_summary, w, w.group_start is not None and not args.ungrouped)
         return
 
+    sys.path.insert(0, ROOT)
+    from workloads import make_config
+
+    t0 = time.time()
+    w = make_config(args.workload, args.block_size)
+    print(f"[bench] workload {w.index} {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} "
+          f"{w.dtype} NB={w.num_blocks} sum(ctx)={w.total_context} generated in {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    pool_baseline = None
+    if not args.no_cpu_baseline:
+        # before any GPU call: the oracle's worker processes are forked from here
+        pool_baseline = cpu_baseline_pool(w, args.cpu_seconds)
+        print(f"[bench] oracle on {pool_baseline['cores']} cores: {pool_baseline['value']} GB/s",
+              file=sys.stderr, flush=True)
+
     import torch
     import paged_kv_cache_159_amd as pkv
-    from workloads import make_config
     from workloads.device import upload
 
     if not torch.cuda.is_available():
@@ -601,12 +670,6 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     pkv.lib()
-
-    t0 = time.time()
-    w = make_config(args.workload, args.block_size)
-    print(f"[bench] workload {w.index} {w.name}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} "
-          f"{w.dtype} NB={w.num_blocks} sum(ctx)={w.total_context} generated in {time.time() - t0:.1f} s",
-          file=sys.stderr, flush=True)
     dw = upload(w, dev)
     if args.swap:
         swap_bench(args, w, dw, dev)
@@ -724,6 +787,7 @@ def main():
     res["hbm_measured"] = hbm_context()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline_all_cores"] = pool_baseline
     print(json.dumps(res), flush=True)
 
 
