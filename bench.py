@@ -769,6 +769,8 @@ def main():
         "seqs_per_s": round(w.num_seqs / (ms * 1e-3), 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "decode_partition_us": round(dec_avg_us, 2),
+        "decode_partition_us_pct": {k: round(float(np.percentile(dec_us, q)), 2)
+                                    for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "decode_logical_kv_gbs": round(logical_b / (dec_avg_us * 1e-6) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
