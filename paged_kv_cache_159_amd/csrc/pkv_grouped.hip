@@ -132,16 +132,17 @@ __device__ __forceinline__ void shared_unit(
   // block (tiles start on multiples of 16 tokens, blocks hold 8 or more).
   // The loads are inline asm so that the compiler does not treat them as LDS
   // writes every later LDS read must wait for; the loop below waits for them
-  // itself (s_waitcnt vmcnt, then a barrier) before a buffer is read.
+  // itself (s_waitcnt vmcnt, then a barrier) before a buffer is read. They are
+  // non-temporal (nt): each prefix row is read once per launch.
   auto issue_tile = [&](int b, uint8_t* buf) {
     const int tw = t0_chunk + b * kTileTokens + 2 * wave;   // wave-uniform
     const int32_t phys = __builtin_amdgcn_readlane(table_lane, tw / BS - blk0);
     const size_t row = ((size_t)phys * BS + (tw % BS) + (lane >> 5)) * kv_dim;
     const uint16_t* ks = key_cache + row + k_elem;
     const uint16_t* vs = value_cache + row + v_elem;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
                  :: "s"(lds_addr(buf + 2 * wave * ROWB)), "v"(ks) : "memory", "m0");
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
                  :: "s"(lds_addr(buf + V_OFF + 2 * wave * ROWB)), "v"(vs) : "memory", "m0");
   };
   // s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima.
