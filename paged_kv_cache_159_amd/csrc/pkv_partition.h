@@ -114,11 +114,17 @@ __device__ __forceinline__ void partition_body(
           ((kTilesPerStep == 1 && BS >= kTileTokens) ? (uint32_t)tb : te) / BS - blk0;
       const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(table_lane, bi);
       const uint32_t off = (te % BS) * row_bytes + col_bytes;
-      // Non-temporal loads: each K/V row is read once per launch, so it
-      // should not displace other lines in the caches (+5-7% at the
-      // LLaMA-7B and long-context decodes).
-      kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                                            reinterpret_cast<const u32x4_nt*>(kpool + (size_t)phys * blk_bytes + off)));
+      // Non-temporal V loads: a row read once per launch should not displace
+      // other lines (+5-7% at the LLaMA-7B and long-context decodes). K stays
+      // cached in the plain call, whose blocks may be shared by several
+      // sequences (beam search through this call keeps more of its cache
+      // hits); tail partitions read private blocks and load both
+      // non-temporally.
+      const char* kp = kpool + (size_t)phys * blk_bytes + off;
+      if constexpr (TAIL)
+        kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(kp)));
+      else
+        kr[i] = *reinterpret_cast<const uint4*>(kp);
       vr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
                                             reinterpret_cast<const u32x4_nt*>(vpool + (size_t)phys * blk_bytes + off)));
     }
