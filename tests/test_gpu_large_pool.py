@@ -144,3 +144,43 @@ def test_large_pool_prefill(head_dim):
     got = device_to_float64(dw.out)
     sel = ~np.isnan(want)
     assert_close(got[sel], want[sel], f"prefill D={head_dim}")
+
+
+@pytest.mark.parametrize("method", ["kernel", "dma", "staged"])
+def test_large_pool_swap(method):
+    """Whole-block swaps between moved device blocks and a pinned host pool,
+    out and back in to other moved blocks, by each of the three methods."""
+    pkv = _pkv()
+    w = make_config(2)
+    dw = upload(w)
+    m = Moved(w, dw)
+    rng = np.random.default_rng(17)
+    ids = rng.permutation(w.key_cache.shape[0])[:96]
+    src, dst = ids[:48], ids[48:]
+    nhost = 64
+    slots = rng.permutation(nhost)[:48]
+    host = []
+    for fill in (0x1234, 0x4321):
+        t = torch.empty((nhost,) + tuple(dw.key_cache.shape[1:]), dtype=dw.key_cache.dtype,
+                        pin_memory=True)
+        t.view(torch.int16).fill_(fill)
+        host.append(t)
+    hk, hv = host
+    hk0, hv0 = device_to_bits(hk).copy(), device_to_bits(hv).copy()
+    as_map = (lambda p: torch.from_numpy(p).cuda()) if method == "kernel" else torch.from_numpy
+    block_bytes = w.block_size * w.num_heads * w.head_dim * 2
+    staging = (torch.empty(4096 + 20 * 2 * block_bytes, dtype=torch.uint8, device="cuda")
+               if method == "staged" else None)
+    pair = lambda a, b: np.stack([a, b], axis=1).astype(np.int32)
+    pkv.swap_blocks(m.key_cache, m.value_cache, hk, hv, as_map(pair(src + m.shift, slots)),
+                    method=method, staging=staging)
+    torch.cuda.synchronize()
+    HK, HV = oracle.swap_blocks(w.key_cache, w.value_cache, hk0, hv0, pair(src, slots))
+    assert np.array_equal(device_to_bits(hk), HK) and np.array_equal(device_to_bits(hv), HV)
+    pkv.swap_blocks(hk, hv, m.key_cache, m.value_cache, as_map(pair(slots, dst + m.shift)),
+                    method=method, staging=staging)
+    torch.cuda.synchronize()
+    K, V = oracle.swap_blocks(HK, HV, w.key_cache, w.value_cache, pair(slots, dst))
+    gk, gv = m.moved_bits()
+    assert np.array_equal(gk, K) and np.array_equal(gv, V), "moved caches differ"
+    say(f"swap {method}: 48 blocks out past 4 GiB and back in to 48 others, bit-exact")
