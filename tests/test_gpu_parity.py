@@ -198,6 +198,25 @@ def test_long_context_sampled():
     assert np.isfinite(got).all()
 
 
+def test_context_131072_tokens():
+    """A 128K-token context (256 partitions of 512 tokens, 8192 table
+    entries) beside a ragged 70,001-token one, 4 heads, bf16: caches
+    bit-exact, every output element against the oracle."""
+    w = make_decode_case([131072, 70001], 4, 128, "bf16", seed=128, max_blocks=8192)
+    check_full_step(w)
+
+
+def test_grouped_long_shared_prefix():
+    """A 20,008-token prefix (1,250 shared blocks in 157 chunks of up to 128
+    tokens on MFMA, then a CoW-copied partial block) for 2 prompts x 4
+    samples, suffixes up to 300 tokens: one merge over 158 partial slots per
+    (sequence, head)."""
+    from workloads import make_shared_case
+    w = make_shared_case(2, 4, 20008, 1, 300, 4, 128, "f16", seed=20008)
+    assert (w.shared_blocks == 1250).all() and len(w.copy_pairs) == 6
+    check_grouped(w)
+
+
 EDGE_CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 1536, 2047,
             2048]
 
