@@ -263,7 +263,8 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     // current stage does not read, and the stage loop waits for them itself
     // (s_waitcnt vmcnt(0), then a barrier) before that buffer is read. Loads
     // unknown to the compiler only make its own vmcnt waits more
-    // conservative (vector loads complete in order).
+    // conservative (vector loads complete in order). m0 (the DMA's LDS
+    // address) is set in the same statement and used by nothing else here.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
