@@ -133,9 +133,7 @@ __device__ __forceinline__ void shared_unit(
   // The loads are inline asm so that the compiler does not treat them as LDS
   // writes every later LDS read must wait for; the loop below waits for them
   // itself (s_waitcnt vmcnt, then a barrier) before a buffer is read. They are
-  // non-temporal (nt): each prefix row is read once per launch. Each statement
-  // sets m0 (the DMA's LDS address) itself; no compiler-generated code in these
-  // kernels uses m0, so hipcc's warning about the m0 clobber changes nothing.
+  // non-temporal (nt): each prefix row is read once per launch.
   auto issue_tile = [&](int b, uint8_t* buf) {
     const int tw = t0_chunk + b * kTileTokens + 2 * wave;   // wave-uniform
     const int32_t phys = __builtin_amdgcn_readlane(table_lane, tw / BS - blk0);
