@@ -160,8 +160,8 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens,
 
 /*
  * Workspace bytes paged_attention_decode_grouped needs: fp32 partials of every
- * shared-prefix chunk (128 tokens) and every tail partition of every
- * (sequence, head), then one int32 per sequence. Returns 0 when the arguments
+ * shared-prefix chunk (128 tokens) and every tail partition (512 tokens) of
+ * every (sequence, head), then one int32 per sequence. Returns 0 when the arguments
  * are invalid.
  */
 size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int head_dim,

@@ -310,7 +310,8 @@ hipError_t grouped_t(const DecodeArgs& a, hipStream_t st) {
 
 template <typename T, int D, int BS>
 hipError_t grouped_b(const DecodeArgs& a, hipStream_t st) {
-  return a.part_tokens == 256 ? grouped_t<T, D, 256, BS>(a, st) : grouped_t<T, D, 512, BS>(a, st);
+  // tail partitions are always 512 tokens
+  return a.part_tokens == 512 ? grouped_t<T, D, 512, BS>(a, st) : hipErrorInvalidValue;
 }
 
 template <typename T, int D>

@@ -127,10 +127,9 @@ def test_merge_validation(L):
 
 def _expected_grouped_workspace(S, H, D, MB, bs=16):
     """Chunk slots of 8 tiles of 16 shared tokens, then the tail partitions
-    (same partition rule as the plain call); one workspace layout."""
+    (always 512 tokens in the grouped call); one workspace layout."""
     tokens = MB * bs
-    pt = 256 if tokens <= 4096 else 512
-    n = S * H * (-(-tokens // 128) + -(-tokens // pt))
+    n = S * H * (-(-tokens // 128) + -(-tokens // 512))
     return ((n * 8 + 255) // 256) * 256 + n * D * 4 + 4 * S
 
 
