@@ -55,8 +55,40 @@ __device__ __forceinline__ void partition_body(
   const int groups = (H + HG - 1) / HG;
   const int g = wg % groups;
   const int sp = wg / groups;
-  const int s = sp % num_seqs;
-  const int p = sp / num_seqs;
+  int s = sp % num_seqs;
+  int p = sp / num_seqs;
+  if constexpr (!TAIL) {
+    // The grid holds num_parts partitions of every sequence, most of them
+    // past a short context. For batches of up to 64 sequences the workgroups
+    // take the real partitions in compact partition-major order (the r-th
+    // workgroup of partition index p takes the r-th sequence that has a
+    // partition p, ranked by ballot over one context length per lane), so
+    // every empty workgroup sits at the end of the grid instead of holding a
+    // slot between real ones.
+    if (num_seqs <= 64) {
+      const int ln = threadIdx.x & 63;
+      const int cl = ln < num_seqs ? context_lens[ln] : 0;
+      const int np = (cl + PT - 1) / PT;   // partitions of sequence ln
+      int rem = sp;
+      s = -1;
+      for (p = 0;; ++p) {
+        const uint64_t m = __ballot(np > p);
+        const int cnt = __popcll(m);
+        if (cnt == 0) break;   // sp is past every real partition
+        if (rem < cnt) {
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const uint64_t sel = __ballot((((m >> ln) & 1ull) != 0) && (int)rank == rem);
+          s = __ffsll((unsigned long long)sel) - 1;
+          break;
+        }
+        rem -= cnt;
+      }
+      s = __builtin_amdgcn_readfirstlane(s);
+      p = __builtin_amdgcn_readfirstlane(p);
+      if (s < 0) return;
+    }
+  }
   const int ctx = context_lens[s];
   int tok0 = 0;   // first token this launch covers for sequence s
   if constexpr (TAIL)
