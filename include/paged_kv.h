@@ -308,11 +308,13 @@ int swap_blocks_dma(const void* src_key, const void* src_value, void* dst_key, v
  * mapping order in chunks that fit `staging`, all on `stream`.
  *   block_mapping  int32 [num_pairs][2], HOST memory, read during the call;
  *                  every id is checked against its pool (PKV_ERR_SHAPE).
- *   staging        device memory, 256-byte aligned: first the scatter mapping
- *                  (num_pairs * 8 bytes, rounded up to 256), then a chunk of
- *                  (staging_bytes - that) / (2 * block_bytes) K and V slots
- *                  (block_bytes = block_size * num_heads * head_dim * 2); at
- *                  least one slot, else PKV_ERR_WORKSPACE.
+ *   staging        device memory, 256-byte aligned: a chunk of
+ *                  staging_bytes / (2 * block_bytes) K slots followed by as
+ *                  many V slots (block_bytes = block_size * num_heads *
+ *                  head_dim * 2); at least one slot, else PKV_ERR_WORKSPACE.
+ * The destination ids of each scatter launch travel in the launch's own
+ * kernel arguments (up to 896 pairs per launch), so no host buffer outlives
+ * the call and the enqueued work may be captured in a HIP graph.
  * Pools and staging as for swap_blocks (PKV_ERR_MEMORY otherwise).
  */
 int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key,

@@ -7,7 +7,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <vector>
 
 #include "paged_kv.h"
 #include "pkv_device.h"
@@ -568,33 +567,20 @@ int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key
     if (sb < 0 || sb >= src_num_blocks || db < 0 || db >= dst_num_blocks) return PKV_ERR_SHAPE;
   }
   const size_t block_bytes = (size_t)block_size * num_heads * head_dim * sizeof(uint16_t);
-  // Staging: [the scatter mapping of every pair, 256-byte aligned][K slots]
-  // [V slots]; the mapping goes up once, the slots are reused chunk by chunk.
-  const size_t map_bytes = ((size_t)num_pairs * 2 * sizeof(int32_t) + 255) & ~(size_t)255;
-  if (staging_bytes < map_bytes + 2 * block_bytes) return PKV_ERR_WORKSPACE;
-  const int cap = (int)std::min<size_t>((staging_bytes - map_bytes) / (2 * block_bytes),
-                                        (size_t)num_pairs);
+  // Staging: [K slots][V slots], reused chunk by chunk.
+  if (staging_bytes < 2 * block_bytes) return PKV_ERR_WORKSPACE;
+  const int cap = (int)std::min<size_t>(staging_bytes / (2 * block_bytes), (size_t)num_pairs);
   const void *sk, *sv, *dk, *dv, *stg;
   bool host_dst = false;
   if ((rc = device_accessible(src_key, block_bytes * src_num_blocks, &sk)) ||
       (rc = device_accessible(src_value, block_bytes * src_num_blocks, &sv)) ||
       (rc = device_accessible(dst_key, block_bytes * dst_num_blocks, &dk, &host_dst)) ||
       (rc = device_accessible(dst_value, block_bytes * dst_num_blocks, &dv, &host_dst)) ||
-      (rc = device_accessible(staging, map_bytes + 2 * (size_t)cap * block_bytes, &stg)))
+      (rc = device_accessible(staging, 2 * (size_t)cap * block_bytes, &stg)))
     return rc;
-  char* st_map = static_cast<char*>(const_cast<void*>(stg));
-  char* st_k = st_map + map_bytes;
+  char* st_k = static_cast<char*>(const_cast<void*>(stg));
   char* st_v = st_k + (size_t)cap * block_bytes;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Scatter mapping: pair i moves staging slot i % cap to its destination.
-  std::vector<int32_t> scatter(2 * (size_t)num_pairs);
-  for (int i = 0; i < num_pairs; ++i) {
-    scatter[2 * i] = i % cap;
-    scatter[2 * i + 1] = block_mapping[2 * i + 1];
-  }
-  if (hipMemcpyAsync(st_map, scatter.data(), scatter.size() * sizeof(int32_t),
-                     hipMemcpyHostToDevice, st) != hipSuccess)
-    return PKV_ERR_LAUNCH;
   for (int c0 = 0; c0 < num_pairs; c0 += cap) {
     const int n = std::min(cap, num_pairs - c0);
     // DMA: each run of consecutive source ids into consecutive staging slots.
@@ -611,13 +597,18 @@ int swap_blocks_staged(const void* src_key, const void* src_value, void* dst_key
         return PKV_ERR_LAUNCH;
       i += r;
     }
-    // Scatter: staging slot -> destination block, one kernel launch per chunk.
-    rc = status_of(pkv::launch_copy_blocks(st_k, st_v, const_cast<void*>(dk),
-                                           const_cast<void*>(dv),
-                                           reinterpret_cast<const int32_t*>(st_map) + 2 * c0, n,
-                                           (int64_t)block_size * num_heads * head_dim,
-                                           /*system_release=*/host_dst, st));
-    if (rc) return rc;
+    // Scatter: staging slot -> destination block, the destination ids of up
+    // to kScatterIds pairs in each launch's arguments.
+    for (int b0 = 0; b0 < n; b0 += pkv::kScatterIds) {
+      const int nb = std::min(pkv::kScatterIds, n - b0);
+      pkv::ScatterIds ids;
+      for (int i = 0; i < nb; ++i) ids.dst[i] = block_mapping[2 * (c0 + b0 + i) + 1];
+      rc = status_of(pkv::launch_scatter_blocks(st_k, st_v, const_cast<void*>(dk),
+                                                const_cast<void*>(dv), ids, nb, b0,
+                                                (int64_t)block_size * num_heads * head_dim,
+                                                /*system_release=*/host_dst, st));
+      if (rc) return rc;
+    }
   }
   return PKV_OK;
 }

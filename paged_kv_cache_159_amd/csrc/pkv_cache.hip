@@ -54,19 +54,10 @@ reshape_and_cache_kernel(const uint4* __restrict__ key, const uint4* __restrict_
   }
 }
 
-template <bool SYSTEM_RELEASE>
-__global__ void __launch_bounds__(kCacheThreads)
-copy_blocks_kernel(const uint4* __restrict__ src_key, const uint4* __restrict__ src_value,
-                   uint4* __restrict__ dst_key, uint4* __restrict__ dst_value,
-                   const int32_t* __restrict__ block_mapping, int64_t block_vecs,
-                   int groups_per_block) {
-  const int g = blockIdx.x % groups_per_block;
-  const int pool = (blockIdx.x / groups_per_block) & 1;
-  const int pair = blockIdx.x / (2 * groups_per_block);
-  const int64_t src = block_mapping[2 * pair];
-  const int64_t dst = block_mapping[2 * pair + 1];
-  const uint4* sp = (pool ? src_value : src_key) + src * block_vecs;
-  uint4* dp = (pool ? dst_value : dst_key) + dst * block_vecs;
+// One workgroup's 16 KiB piece g of a block copy from sp to dp (block_vecs
+// 16-byte vectors per block).
+__device__ __forceinline__ void copy_block_piece(const uint4* __restrict__ sp, uint4* __restrict__ dp,
+                                                 int64_t block_vecs, int g) {
   const int64_t first = (int64_t)g * kCopyVecsPerGroup + threadIdx.x;
   // Loads are unconditional (indices past the block re-read its last vector)
   // and all four are issued before the stores, so they are in flight at once.
@@ -83,6 +74,40 @@ copy_blocks_kernel(const uint4* __restrict__ src_key, const uint4* __restrict__ 
   if (e1 < block_vecs) dp[e1] = v1;
   if (e2 < block_vecs) dp[e2] = v2;
   if (e3 < block_vecs) dp[e3] = v3;
+}
+
+template <bool SYSTEM_RELEASE>
+__global__ void __launch_bounds__(kCacheThreads)
+copy_blocks_kernel(const uint4* __restrict__ src_key, const uint4* __restrict__ src_value,
+                   uint4* __restrict__ dst_key, uint4* __restrict__ dst_value,
+                   const int32_t* __restrict__ block_mapping, int64_t block_vecs,
+                   int groups_per_block) {
+  const int g = blockIdx.x % groups_per_block;
+  const int pool = (blockIdx.x / groups_per_block) & 1;
+  const int pair = blockIdx.x / (2 * groups_per_block);
+  const int64_t src = block_mapping[2 * pair];
+  const int64_t dst = block_mapping[2 * pair + 1];
+  copy_block_piece((pool ? src_value : src_key) + src * block_vecs,
+                   (pool ? dst_value : dst_key) + dst * block_vecs, block_vecs, g);
+  if constexpr (SYSTEM_RELEASE) __threadfence_system();
+}
+
+// Scatter of consecutive staging slots to listed destination blocks: pair i
+// copies slot slot0 + i to block ids.dst[i]. The ids travel in the kernel's
+// arguments, which the launch copies, so no host buffer has to outlive the
+// enqueue (and a captured launch replays with the same ids).
+template <bool SYSTEM_RELEASE>
+__global__ void __launch_bounds__(kCacheThreads)
+scatter_blocks_kernel(const uint4* __restrict__ src_key, const uint4* __restrict__ src_value,
+                      uint4* __restrict__ dst_key, uint4* __restrict__ dst_value, ScatterIds ids,
+                      int slot0, int64_t block_vecs, int groups_per_block) {
+  const int g = blockIdx.x % groups_per_block;
+  const int pool = (blockIdx.x / groups_per_block) & 1;
+  const int pair = blockIdx.x / (2 * groups_per_block);
+  const int64_t src = slot0 + pair;
+  const int64_t dst = ids.dst[pair];
+  copy_block_piece((pool ? src_value : src_key) + src * block_vecs,
+                   (pool ? dst_value : dst_key) + dst * block_vecs, block_vecs, g);
   if constexpr (SYSTEM_RELEASE) __threadfence_system();
 }
 
@@ -113,6 +138,25 @@ hipError_t launch_copy_blocks(const void* src_key, const void* src_value, void* 
   else
     hipLaunchKernelGGL(copy_blocks_kernel<false>, dim3(grid), dim3(kCacheThreads), 0, stream, sk,
                        sv, dk, dv, block_mapping, block_vecs, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_blocks(const void* src_key, const void* src_value, void* dst_key,
+                                 void* dst_value, const ScatterIds& ids, int num_pairs, int slot0,
+                                 int64_t block_elems, bool system_release, hipStream_t stream) {
+  const int64_t block_vecs = block_elems / 8;
+  const int groups = (int)((block_vecs + kCopyVecsPerGroup - 1) / kCopyVecsPerGroup);
+  const unsigned grid = (unsigned)num_pairs * 2u * (unsigned)groups;
+  auto* sk = static_cast<const uint4*>(src_key);
+  auto* sv = static_cast<const uint4*>(src_value);
+  auto* dk = static_cast<uint4*>(dst_key);
+  auto* dv = static_cast<uint4*>(dst_value);
+  if (system_release)
+    hipLaunchKernelGGL(scatter_blocks_kernel<true>, dim3(grid), dim3(kCacheThreads), 0, stream, sk,
+                       sv, dk, dv, ids, slot0, block_vecs, groups);
+  else
+    hipLaunchKernelGGL(scatter_blocks_kernel<false>, dim3(grid), dim3(kCacheThreads), 0, stream,
+                       sk, sv, dk, dv, ids, slot0, block_vecs, groups);
   return hipGetLastError();
 }
 

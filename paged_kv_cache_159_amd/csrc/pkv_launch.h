@@ -90,4 +90,18 @@ hipError_t launch_copy_blocks(const void* src_key, const void* src_value, void* 
                               void* dst_value, const int32_t* block_mapping, int num_pairs,
                               int64_t block_elems, bool system_release, hipStream_t stream);
 
+// Destination block ids of one scatter launch (swap_blocks_staged), passed
+// by value in the kernel arguments: 896 ids keep the arguments under 4 KiB.
+constexpr int kScatterIds = 896;
+struct ScatterIds {
+  int32_t dst[kScatterIds];
+};
+
+// Copies staging slots slot0 .. slot0 + num_pairs - 1 of (src_key, src_value)
+// to blocks ids.dst[0 .. num_pairs) of (dst_key, dst_value); num_pairs <=
+// kScatterIds.
+hipError_t launch_scatter_blocks(const void* src_key, const void* src_value, void* dst_key,
+                                 void* dst_value, const ScatterIds& ids, int num_pairs, int slot0,
+                                 int64_t block_elems, bool system_release, hipStream_t stream);
+
 }  // namespace pkv

@@ -8,12 +8,10 @@ namespace pkv {
 
 constexpr int kWaves = 8;
 typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
-#ifndef PKV_TILES_PER_STEP
-#define PKV_TILES_PER_STEP 1
-#endif
 // 16-token tiles each loop step covers: every wave has 2 * kTilesPerStep rows
-// of K and V in flight per step.
-constexpr int kTilesPerStep = PKV_TILES_PER_STEP;
+// of K and V in flight per step (two tiles per step measured within +-0.5
+// points of one at the LLaMA-7B, shared-prefix and long-context decodes).
+constexpr int kTilesPerStep = 1;
 
 // LDS bytes partition_body needs: per wave and head (max, sum), and per wave a
 // head group's accumulators.

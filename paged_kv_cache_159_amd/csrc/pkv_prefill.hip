@@ -61,32 +61,19 @@ namespace pkv {
 // tiles (one wave per SIMD at 274 registers) 222; 8 x 1 373; 128-key stages
 // 330; the table copied to LDS, or V^T operands read once for both query
 // tiles, no gain.
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 8
-#endif
-#ifndef PKV_PREFILL_QW
-#define PKV_PREFILL_QW 2
-#endif
-#ifndef PKV_PREFILL_KEYS
-#define PKV_PREFILL_KEYS 64
-#endif
-constexpr int kPrefillWaves = PKV_PREFILL_WAVES;
-constexpr int kPrefillQW = PKV_PREFILL_QW;                           // 16-row tiles per wave
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillQW = 2;                                        // 16-row tiles per wave
 constexpr int kPrefillRows = 16 * kPrefillQW * kPrefillWaves;        // rows per workgroup
-constexpr int kPrefillKeys = PKV_PREFILL_KEYS;                       // keys per LDS stage
+constexpr int kPrefillKeys = 64;                                     // keys per LDS stage
 // Bytes of one V^T row: the keys plus padding that keeps the 8-byte operand
 // reads of 32 lanes (16 dims x 2 key groups) on distinct LDS banks.
-constexpr int kVtRow = kPrefillKeys * 2 + (kPrefillKeys == 64 ? 8 : 16);
-#ifndef PKV_VT_SWIZZLE
-#define PKV_VT_SWIZZLE 1
-#endif
+constexpr int kVtRow = kPrefillKeys * 2 + 8;
 // Byte offset of key k in V^T row d: groups of 4 keys (one 8-byte MFMA
 // operand read) are XOR-swizzled by bits 5..6 of d, so the transposed 2-byte
 // stores of a wave (16 column pieces of 8 dims each, 4 keys) fall on distinct
 // LDS banks; the 16 lanes of an operand read share d >> 5, hence one swizzle.
 __device__ __forceinline__ int vt_key_offset(int d, int k) {
-  if (PKV_VT_SWIZZLE) return ((((k >> 2) ^ ((d >> 5) & 3)) << 2) | (k & 3)) * 2;
-  return k * 2;
+  return ((((k >> 2) ^ ((d >> 5) & 3)) << 2) | (k & 3)) * 2;
 }
 
 template <int D>
@@ -117,17 +104,14 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   constexpr int PIECES = kPrefillKeys * D / 8;    // 16-byte pieces of K (or V) per stage
   constexpr int PER_THREAD = PIECES / THREADS;
   static_assert(PIECES % THREADS == 0, "whole pieces per thread");
-#ifndef PKV_PREFILL_DBUF
-#define PKV_PREFILL_DBUF 1
-#endif
-  constexpr int NBUF = PKV_PREFILL_DBUF ? 2 : 1;
+  constexpr int NBUF = 2;   // register-staged stages alternate between two buffers
   // Direct staging (head size 128): K and V rows go from global memory
   // straight into LDS (one 16-byte load per lane, lane l landing at the
   // instruction's base + 16 l), unpadded 256-byte rows with XOR-swizzled
   // 16-byte pieces; V stays row-major and P.V operands come from transposing
   // LDS reads. Other head sizes stage through registers into padded K rows
   // and a 2-byte-element V^T.
-  constexpr bool kDirect = D == 128 && kPrefillKeys == 64 && kPrefillWaves == 8;
+  constexpr bool kDirect = D == 128;
   constexpr int kDirectRow = 2 * D;                       // 256 bytes
   constexpr int kDirectStage = 2 * kPrefillKeys * kDirectRow;   // K rows, then V rows
   // A ring of three stage buffers: the loads of stages st + 1 and st + 2 fly
@@ -286,19 +270,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     __syncthreads();
   } else {
     load_stage(0);
-    if constexpr (NBUF == 2) {
-      store_stage(0);
-      __syncthreads();
-      if (nstages > 1) load_stage(1);
-    }
+    store_stage(0);
+    __syncthreads();
+    if (nstages > 1) load_stage(1);
   }
   for (int st = 0; st < nstages; ++st) {
-    if constexpr (!kDirect && NBUF == 1) {
-      __syncthreads();                // every wave is done with the previous stage
-      store_stage(0);
-      __syncthreads();
-      if (st + 1 < nstages) load_stage(st + 1);
-    }
     const uint8_t* s_k;
     const uint8_t* s_vt;
     if constexpr (kDirect) {
@@ -312,8 +288,8 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       s_k = cur;
       s_vt = cur + kPrefillKeys * kDirectRow;
     } else {
-      s_k = s_kbuf[NBUF == 2 ? (st & 1) : 0];
-      s_vt = s_vtbuf[NBUF == 2 ? (st & 1) : 0];
+      s_k = s_kbuf[st & 1];
+      s_vt = s_vtbuf[st & 1];
     }
     if (wrow0 < qn) {                 // a wave past the chunk's end only helps staging
 #pragma unroll
@@ -518,7 +494,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       else
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-    } else if constexpr (NBUF == 2) {
+    } else {
       // The other buffer was last read in stage st - 1; every wave has
       // passed the barrier that ended it.
       if (st + 1 < nstages) store_stage((st + 1) & 1);

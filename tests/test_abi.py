@@ -311,7 +311,7 @@ def test_swap_blocks_staged_validation(L):
     m = (ctypes.c_int32 * 6)(0, 1, 1, 2, 7, 3)
     mp = ctypes.addressof(m)
     block_bytes = 16 * 4 * 64 * 2
-    big = 256 + 10 * 2 * block_bytes
+    big = 10 * 2 * block_bytes
     base = [P, P, P, P, mp, 3, 4, 64, 8, 4, 16, 0, 0x20000, big, 0]
 
     def call(i, v):
@@ -326,6 +326,6 @@ def test_swap_blocks_staged_validation(L):
         assert call(i, 0) == NULL, i
     assert call(12, 0x20000 + 16) == ALIGN        # staging must be 256-byte aligned
     assert call(8, 7) == SHAPE                    # source id 7 outside a 7-block pool
-    assert call(13, 256 + 2 * block_bytes - 1) == WS
+    assert call(13, 2 * block_bytes - 1) == WS
     assert call(5, 0) == OK
     assert f(*base) == MEMORY
