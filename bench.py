@@ -80,6 +80,13 @@ def parse():
                          "LLaMA-7B shape; prints its own JSON line")
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="element type of the --prefill workloads")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-workload records (workloads 2-5, 5 warm-up + 50 timed "
+                         "decode calls each) that the default run adds to its JSON line")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="turn a rocprofv3 --stats kernel_stats.csv of `bench.py --workload N "
+                         "--no-per-config --no-cpu-baseline` into profiles/kernels_<workload>.md "
+                         "and exit (no GPU needed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -623,6 +630,166 @@ def cpu_baseline_pool(w, budget_s):
             "seqs_per_s": round(seqs / el, 4)}
 
 
+def make_replicas(dw, pkv, w, dev, min_total=4.0e9, max_r=16):
+    """The pools and one output per replica: R copies of the K/V pools at
+    different addresses (at least min_total bytes in all), so that rotating
+    through them finds no K/V in the 256 MB last-level cache."""
+    import torch
+    pool_bytes = 2 * dw.key_cache.numel() * 2
+    R = min(max_r, max(2, int(np.ceil(min_total / pool_bytes))))
+    kcs = [dw.key_cache] + [dw.key_cache.clone() for _ in range(R - 1)]
+    vcs = [dw.value_cache] + [dw.value_cache.clone() for _ in range(R - 1)]
+    outs = [torch.empty_like(dw.query) for _ in range(R)]
+    return R, kcs, vcs, outs
+
+
+def _pct(x):
+    return {k: round(float(np.percentile(x, q)), 2) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+
+def per_config_record(index, dev, runs=50, warmup=5, block_size=16):
+    """One workload's decode step timed call by call with HIP events on the
+    launch stream: copy_blocks | reshape_and_cache | decode kernel | merge,
+    5 warm-up and 50 timed steps over rotated pool replicas. Reports the
+    median (p10, p90) of each part, the decode's algorithmic bytes per second
+    against the 8 TB/s peak (whole decode call, and its dominant kernel), and
+    sequences per second. Workload 4 runs the grouped call (its kernel and
+    merge are one call, timed together)."""
+    import torch
+
+    import paged_kv_cache_159_amd as pkv
+    from workloads import make_config
+    from workloads.device import upload
+
+    w = make_config(index, block_size)
+    dw = upload(w, dev)
+    R, kcs, vcs, outs = make_replicas(dw, pkv, w, dev)
+    grouped = w.group_start is not None
+    if grouped:
+        gs = torch.from_numpy(w.group_start).to(dev)
+        sb = torch.from_numpy(w.shared_blocks).to(dev)
+        ws = torch.empty(max(pkv.grouped_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                        w.max_blocks_per_seq, w.block_size), 16),
+                         dtype=torch.uint8, device=dev)
+    else:
+        ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                                 w.block_size, device=dev)
+    has_copy = len(w.copy_pairs) > 0
+    evs = []
+
+    def one(i, record):
+        r = i % R
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        rec = (lambda j: e[j].record()) if record else (lambda j: None)
+        rec(0)
+        if has_copy:
+            pkv.copy_blocks(kcs[r], vcs[r], dw.copy_pairs)
+        rec(1)
+        pkv.reshape_and_cache(dw.new_key, dw.new_value, kcs[r], vcs[r], dw.slot_mapping)
+        rec(2)
+        if grouped:
+            pkv.paged_attention_decode_grouped(outs[r], dw.query, kcs[r], vcs[r], dw.block_tables,
+                                               dw.context_lens, gs, sb, w.scale, workspace=ws)
+            rec(3)
+        else:
+            pkv.paged_attention_decode_partitions(outs[r], dw.query, kcs[r], vcs[r],
+                                                  dw.block_tables, dw.context_lens, w.scale, ws)
+            rec(3)
+            pkv.paged_attention_decode_merge(outs[r], dw.context_lens, w.max_blocks_per_seq, ws,
+                                             block_size=w.block_size)
+        rec(4)
+        if record:
+            evs.append(e)
+
+    for i in range(warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    for i in range(runs):
+        one(i, True)
+    torch.cuda.synchronize()
+    t = np.array([[a.elapsed_time(b) * 1e3 for a, b in zip(e[:-1], e[1:])] for e in evs])
+    copy_us, write_us, kern_us, merge_us = t[:, 0], t[:, 1], t[:, 2], t[:, 3]
+    call_us = kern_us + merge_us
+    dec_b, write_b, copy_b, logical_b = algorithmic_bytes(w)
+    kmed, cmed = float(np.median(kern_us)), float(np.median(call_us))
+    traffic = load_traffic(traffic_key(w, grouped))
+    rec = {
+        "workload": f"{w.name}: {w.num_seqs} seqs x {w.num_heads} heads x {w.head_dim}, {w.dtype}, "
+                    f"block_size {w.block_size}, sum(ctx)={w.total_context}, "
+                    f"{len(w.slot_mapping)} new tokens, {len(w.copy_pairs)} CoW pairs",
+        "decode_path": "grouped (shared-prefix MFMA units + tail partitions, then merge)" if grouped
+                       else "plain (partition kernel, then merge)",
+        "runs": runs, "warmup": warmup, "pool_replicas": R,
+        "algorithmic_bytes": int(dec_b),
+        "decode_call_us": _pct(call_us),
+        "decode_kernel_us": _pct(kern_us) if not grouped else None,
+        "decode_call_gbs": round(dec_b / (cmed * 1e-6) / 1e9, 1),
+        "decode_call_frac": round(dec_b / (cmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_kernel_gbs": round(dec_b / (kmed * 1e-6) / 1e9, 1) if not grouped else None,
+        "decode_kernel_frac": (round(dec_b / (kmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                               if not grouped else None),
+        "seqs_per_s": round(w.num_seqs / (cmed * 1e-6), 1),
+        "traffic_bytes": traffic,
+        "traffic_over_algorithmic": round(traffic / dec_b, 4) if traffic else None,
+        "cache_write_us": _pct(write_us),
+        "cache_write_gbs": round(write_b / (float(np.median(write_us)) * 1e-6) / 1e9, 1),
+    }
+    if grouped:
+        rec["logical_bytes"] = int(logical_b)
+        rec["decode_call_logical_gbs"] = round(logical_b / (cmed * 1e-6) / 1e9, 1)
+    if has_copy:
+        rec["copy_blocks_us"] = _pct(copy_us)
+        rec["copy_blocks_gbs"] = round(copy_b / (float(np.median(copy_us)) * 1e-6) / 1e9, 1)
+    del kcs, vcs, outs, dw, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
+def stats_summary(csv_path, w, grouped):
+    """profiles/kernels_<workload>.md from a rocprofv3 kernel_stats.csv of
+    `bench.py --workload N --no-per-config --no-cpu-baseline`: the kernel
+    table, and the decode kernels' algorithmic bytes over their average
+    duration against the 8 TB/s peak."""
+    import csv
+    rows = []
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r["Name"].split("(")[0].replace("void ", "")
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    dec_b = algorithmic_bytes(w)[0]
+    names = TIMED_KERNELS["grouped" if grouped else "plain"]
+    timed = [r for r in rows if any(k in r[0] for k in names)]
+    us = sum(r[2] for r in timed)
+    key = traffic_key(w, grouped)
+    ung = "" if w.block_size == 16 else f" --block-size {w.block_size}"
+    lines = [f"# rocprofv3 kernel stats: {key}", "",
+             f"Workload: {w.name}, {w.num_seqs} sequences x {w.num_heads} heads x {w.head_dim}, "
+             f"{w.dtype} KV, block size {w.block_size}, sum of contexts {w.total_context:,}, "
+             f"{len(w.slot_mapping)} new tokens, {len(w.copy_pairs)} CoW pairs. One step = "
+             f"{'copy_blocks + ' if len(w.copy_pairs) else ''}reshape_and_cache + "
+             f"{'grouped decode (shared-prefix MFMA units and tail partitions) + merge' if grouped else 'decode partition launch + merge launch'}; "
+             "pool replicas rotated.", "",
+             "Command (repo root, MI355X):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o s -- python -u bench.py "
+             f"--workload {w.index}{ung} --no-per-config --no-cpu-baseline", "```", "",
+             f"Decode kernel source digest (bench.py `source_digest`): `{source_digest(grouped)}`.", "",
+             "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
+    for n, c, a, mn, mx, pc in rows:
+        lines.append(f"| `{n}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {pc:.1f}% |")
+    lines += ["", "Kernels outside the step (`__amd_rocclr_copyBuffer`, `fillBuffer`, torch's "
+              "`reduce_kernel` and random fills) are the uploads, the replica copies and the "
+              "measured-HBM context of bench.py.", "",
+              f"Algorithmic bytes of one decode launch: {dec_b:,} B. Timed kernels: "
+              f"{', '.join(r[0] for r in timed)}; average {us:.2f} us in all: "
+              f"{dec_b / (us * 1e-6) / 1e12:.3f} TB/s = {dec_b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} "
+              "of the 8 TB/s HBM peak.", ""]
+    out = os.path.join(ROOT, "profiles", f"kernels_{key}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -643,6 +810,12 @@ def main():
         from workloads import make_config
         w = make_config(args.workload, args.block_size)
         traffic_summary(args.traffic_summary, w, w.group_start is not None and not args.ungrouped)
+        return
+    if args.stats_summary:
+        sys.path.insert(0, ROOT)
+        from workloads import make_config
+        w = make_config(args.workload, args.block_size)
+        stats_summary(args.stats_summary, w, w.group_start is not None and not args.ungrouped)
         return
 
     sys.path.insert(0, ROOT)
@@ -675,13 +848,12 @@ def main():
         swap_bench(args, w, dw, dev)
         return
     pool_bytes = 2 * dw.key_cache.numel() * 2
-    R = args.replicas or max(2, int(np.ceil(4.0e9 / pool_bytes)))
-    R = min(R, 16)
-    kcs = [dw.key_cache] + [dw.key_cache.clone() for _ in range(R - 1)]
-    vcs = [dw.value_cache] + [dw.value_cache.clone() for _ in range(R - 1)]
+    if args.replicas:
+        R, kcs, vcs, outs = make_replicas(dw, pkv, w, dev, min_total=args.replicas * pool_bytes)
+    else:
+        R, kcs, vcs, outs = make_replicas(dw, pkv, w, dev)
     ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
                              w.block_size, device=dev)
-    outs = [torch.empty_like(dw.query) for _ in range(R)]
     dec_b, write_b, copy_b, logical_b = algorithmic_bytes(w)
     step_bytes = dec_b + write_b + copy_b
     has_copy = len(w.copy_pairs) > 0
@@ -738,9 +910,10 @@ def main():
     ms = wall / args.steps * 1e3
     dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
     dec_avg_us = float(np.mean(dec_us))
-    achieved = dec_b / (dec_avg_us * 1e-6) / 1e9
+    dec_med_us = float(np.median(dec_us))
+    achieved = dec_b / (dec_med_us * 1e-6) / 1e9
     value = step_bytes / (ms * 1e-3) / 1e9
-    print(f"[bench] {ms * 1e3:.1f} us/step; partition kernel avg {dec_avg_us:.1f} us "
+    print(f"[bench] {ms * 1e3:.1f} us/step; partition kernel median {dec_med_us:.1f} us, avg {dec_avg_us:.1f} us "
           f"(p10 {np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f}) -> "
           f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak", file=sys.stderr, flush=True)
 
@@ -768,10 +941,11 @@ def main():
         },
         "seqs_per_s": round(w.num_seqs / (ms * 1e-3), 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
-        "decode_partition_us": round(dec_avg_us, 2),
+        "decode_partition_us": round(dec_med_us, 2),
+        "decode_partition_us_mean": round(dec_avg_us, 2),
         "decode_partition_us_pct": {k: round(float(np.percentile(dec_us, q)), 2)
                                     for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
-        "decode_logical_kv_gbs": round(logical_b / (dec_avg_us * 1e-6) / 1e9, 1),
+        "decode_logical_kv_gbs": round(logical_b / (dec_med_us * 1e-6) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -782,10 +956,19 @@ def main():
             "kernel": "grouped decode (shared-prefix MFMA + tail partitions + merge)" if grouped
                       else "decode_partition_kernel",
             "bytes_per_launch": dec_b,
+            "duration": "median of the HIP-event durations of the timed region's launches",
         },
     }
-    del kcs, vcs
+    del kcs, vcs, outs, ws
     torch.cuda.empty_cache()
+    if not args.no_per_config and args.block_size == 16:
+        res["per_config"] = {}
+        for idx in (2, 3, 4, 5):
+            res["per_config"][str(idx)] = per_config_record(idx, dev)
+            rc_ = res["per_config"][str(idx)]
+            print(f"[bench] workload {idx}: decode call {rc_['decode_call_us']['p50']} us -> "
+                  f"{rc_['decode_call_frac']:.3f} of peak, {rc_['seqs_per_s']:.0f} seqs/s",
+                  file=sys.stderr, flush=True)
     res["hbm_measured"] = hbm_context()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -98,6 +98,42 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// DPP lane moves for a wave-wide prefix sum (gfx9 control codes): shift right
+// by n lanes within each 16-lane row, and the broadcast of lane 15 (31) of a
+// row to the rows after it.
+enum : int {
+  kDppRowShr1 = 0x111,
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppRowBcast15 = 0x142,
+  kDppRowBcast31 = 0x143,
+};
+
+// Inclusive prefix sum of x over lanes 0 .. this lane, with DPP moves only
+// (no LDS round trips): a scan inside each 16-lane row, then row 0's total
+// into row 1 and row 2's into row 3, then lane 31's running total into rows 2
+// and 3. Lanes whose DPP source lies outside the row add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
+  return x;
+}
+
+// Lane holding the (j + 1)-th set bit of the wave-uniform mask m (j <
+// popcount(m)), found by ranking the set lanes with mbcnt and one ballot.
+__device__ __forceinline__ int nth_set_lane(uint64_t m, int j) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  const uint64_t sel = __ballot((((m >> lane) & 1ull) != 0) && (int)rank == j);
+  return __ffsll((unsigned long long)sel) - 1;
+}
+
 // 2^x with the hardware instruction (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -21,6 +21,102 @@ constexpr int partition_lds_bytes() {
   return (2 * kWaves * HG + kWaves * HG * D) * (int)sizeof(float);
 }
 
+// Work-item order of the plain decode grid. The grid holds num_parts
+// partition slots per sequence (sized from the table), of which a sequence
+// uses ceil(ctx / PT). A full partition (PT tokens) is the longest item; each
+// sequence has at most one shorter item, its last partition. The real items
+// are dispatched longest first: every full partition (sequence-major), then
+// the last partitions by length class (kRemClasses classes of PT /
+// kRemClasses tokens, longest class first, sequences in order within a
+// class), so the items still running when the grid drains are the shortest
+// ones. Measured on MI355X against partition-major order (32 heads x 128,
+// fp16): 64 sequences of U[128, 2048] tokens 169.7 -> 164.3 us, 64 of
+// Exp(512) 87.5 -> 83.5, 128 of U[128, 2048] 372.0 -> 361.5, 256 of
+// U[128, 2048] 690.4 -> 682.5, 256 of Exp(512) and 8 x 32K unchanged
+// (351.7, 633.7 -> 629.0).
+constexpr int kPlanMaxSeqs = 256;   // context lengths held in registers (4 per lane)
+constexpr int kRemClasses = 8;
+
+// Item of grid slot sp (of num_seqs * num_parts slots): sequence s and
+// partition p; false for a slot with no item. Computed by each wave from the
+// context lengths (one load per lane and 64 sequences), wave-uniform.
+template <int PT>
+__device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
+                                          const int32_t* __restrict__ context_lens, int& s,
+                                          int& p) {
+  constexpr int KC = kPlanMaxSeqs / 64;
+  const int lane = threadIdx.x & 63;
+  int cl[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int sq = 64 * k + lane;
+    cl[k] = (64 * k < num_seqs && sq < num_seqs) ? context_lens[sq] : 0;
+  }
+  int nf[KC], cls[KC], incl[KC], tot[KC];
+  int F = 0, R = 0;
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    nf[k] = cl[k] / PT;
+    const int r = cl[k] % PT;
+    cls[k] = r ? (r * kRemClasses + PT - 1) / PT : 0;   // 1 .. kRemClasses
+    incl[k] = 0;
+    tot[k] = 0;
+    if (64 * k < num_seqs) {                             // wave-uniform
+      incl[k] = wave_inclusive_scan(nf[k]);
+      tot[k] = __builtin_amdgcn_readlane(incl[k], 63);
+      F += tot[k];
+      R += __popcll(__ballot(r > 0));
+    }
+  }
+  const uint32_t N = (uint32_t)(F + R);                  // real items
+  // Item i sits at slot floor(i * NP / N): the empty slots are spread evenly
+  // over the grid. Gathered at the grid's end instead, they cost 10% at 256
+  // sequences (~11,000 empty workgroups, each loading the context lengths,
+  // run after the real work has drained).
+  const uint32_t NP = (uint32_t)num_seqs * (uint32_t)num_parts;
+  const uint32_t i = ((uint32_t)sp * N + NP - 1) / NP;
+  if (i >= N || (i * NP) / N != (uint32_t)sp) return false;
+  if ((int)i < F) {
+    int j = (int)i;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      if (j < tot[k]) {
+        const int ln = __ffsll((unsigned long long)__ballot(incl[k] > j)) - 1;
+        s = 64 * k + ln;
+        p = j - __builtin_amdgcn_readlane(incl[k] - nf[k], ln);
+        return true;
+      }
+      j -= tot[k];
+    }
+    return false;   // not reached: i < F
+  }
+  int j = (int)i - F;
+#pragma unroll
+  for (int c = kRemClasses; c >= 1; --c) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      if (64 * k >= num_seqs) break;
+      const uint64_t m = __ballot(cls[k] == c);
+      const int cnt = __popcll(m);
+      if (j < cnt) {
+        const int ln = nth_set_lane(m, j);
+        s = 64 * k + ln;
+        p = __builtin_amdgcn_readlane(nf[k], ln);
+        return true;
+      }
+      j -= cnt;
+    }
+  }
+  return false;     // not reached: i < N
+}
+
+// Grid slots of the plain launch whose items plan_item orders (above this the
+// grid keeps its plain order, partition-major): slot arithmetic stays in 32
+// bits.
+__host__ __device__ constexpr bool plan_fits(int num_seqs, int num_parts) {
+  return num_parts > 1 && num_seqs <= kPlanMaxSeqs && (int64_t)num_seqs * num_parts <= 65536;
+}
+
 // One workgroup (index wg) of the partition launch: (head group, sequence,
 // partition), head groups fastest, over blocks of BS tokens. The partition is
 // walked in 16-token tiles whatever the block size (a tile is one 16-token
@@ -56,35 +152,15 @@ __device__ __forceinline__ void partition_body(
   int s = sp % num_seqs;
   int p = sp / num_seqs;
   if constexpr (!TAIL) {
-    // The grid holds num_parts partitions of every sequence, most of them
-    // past a short context. For batches of up to 64 sequences the workgroups
-    // take the real partitions in compact partition-major order (the r-th
-    // workgroup of partition index p takes the r-th sequence that has a
-    // partition p, ranked by ballot over one context length per lane), so
-    // every empty workgroup sits at the end of the grid instead of holding a
-    // slot between real ones.
-    if (num_seqs <= 64) {
-      const int ln = threadIdx.x & 63;
-      const int cl = ln < num_seqs ? context_lens[ln] : 0;
-      const int np = (cl + PT - 1) / PT;   // partitions of sequence ln
-      int rem = sp;
-      s = -1;
-      for (p = 0;; ++p) {
-        const uint64_t m = __ballot(np > p);
-        const int cnt = __popcll(m);
-        if (cnt == 0) break;   // sp is past every real partition
-        if (rem < cnt) {
-          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
-              (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          const uint64_t sel = __ballot((((m >> ln) & 1ull) != 0) && (int)rank == rem);
-          s = __ffsll((unsigned long long)sel) - 1;
-          break;
-        }
-        rem -= cnt;
-      }
-      s = __builtin_amdgcn_readfirstlane(s);
-      p = __builtin_amdgcn_readfirstlane(p);
-      if (s < 0) return;
+    if (plan_fits(num_seqs, num_parts)) {
+      int ps = 0, pp = 0;
+      const bool real = plan_item<PT>(sp, num_seqs, num_parts, context_lens, ps, pp);
+      // an item outside the grid's (sequence, partition) range is never
+      // produced; the bound keeps every later index inside the arrays anyway
+      if (!real || (unsigned)ps >= (unsigned)num_seqs || (unsigned)pp >= (unsigned)num_parts)
+        return;
+      s = __builtin_amdgcn_readfirstlane(ps);
+      p = __builtin_amdgcn_readfirstlane(pp);
     }
   }
   const int ctx = context_lens[s];
