@@ -84,9 +84,14 @@ typedef enum {
   PKV_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
   PKV_ERR_MEMORY = -7,      /* swap_blocks: a buffer is not device memory of the current
                                device or pinned host memory, or is smaller than its sizes */
-  PKV_ERR_DATA = -8         /* PAGED_KV_DEBUG=1 only: a data-dependent precondition does not
+  PKV_ERR_DATA = -8,        /* PAGED_KV_DEBUG=1 only: a data-dependent precondition does not
                                hold; nothing was launched */
+  PKV_ERR_SCRATCH = -9      /* paged_attention_decode_noalloc: the call needs more than
+                               PKV_NOALLOC_SCRATCH_BYTES of scratch */
 } pkv_status;
+
+/* Bytes of the fixed per-device scratch array of paged_attention_decode_noalloc. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Library version, major*10000 + minor*100 + patch. */
 int pkv_version(void);
@@ -130,6 +135,28 @@ int paged_attention_decode(void* out, const void* query,
                            int num_seqs, int num_heads, int head_dim, int num_blocks,
                            int block_size, int max_blocks_per_seq, float scale, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_decode for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments and result as paged_attention_decode (the same kernels, so the
+ * output is bit-identical), without a workspace: the split-K partials go to
+ * a fixed device array of PKV_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine). A call whose
+ * partials need more than that (paged_attention_workspace_size(...) >
+ * PKV_NOALLOC_SCRATCH_BYTES) returns PKV_ERR_SCRATCH before touching the
+ * device. Every call on one GPU shares that GPU's array and leaves its
+ * partials in it; nothing in it must start at zero. Calls that overlap on one
+ * GPU (on different streams, or from several threads without ordering) race
+ * on the array and may return wrong results: order them on one stream.
+ */
+int paged_attention_decode_noalloc(void* out, const void* query,
+                                   const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int num_seqs, int num_heads, int head_dim, int num_blocks,
+                                   int block_size, int max_blocks_per_seq, float scale,
+                                   int dtype, void* stream);
 
 /*
  * First of the two launches of paged_attention_decode: one workgroup per

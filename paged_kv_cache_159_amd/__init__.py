@@ -14,6 +14,7 @@ from .ops import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_grouped,
     paged_attention_decode_merge,
+    paged_attention_decode_noalloc,
     paged_attention_decode_partitions,
     paged_attention_prefill,
     reshape_and_cache,

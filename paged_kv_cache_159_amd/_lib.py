@@ -19,6 +19,7 @@ EXPORTS = (
     "pkv_status_string",
     "paged_attention_workspace_size",
     "paged_attention_decode",
+    "paged_attention_decode_noalloc",
     "paged_attention_decode_partitions",
     "paged_attention_decode_merge",
     "paged_attention_grouped_workspace_size",
@@ -34,7 +35,9 @@ EXPORTS = (
 PKV_F16, PKV_BF16 = 0, 1
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_UNSUPPORTED",
           -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_LAUNCH", -6: "PKV_ERR_ALIGN", -7: "PKV_ERR_MEMORY",
-          -8: "PKV_ERR_DATA"}
+          -8: "PKV_ERR_DATA", -9: "PKV_ERR_SCRATCH"}
+# Bytes of paged_attention_decode_noalloc's fixed per-device scratch array.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -48,6 +51,7 @@ _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i]),
     "paged_attention_workspace_size": (_z, [_i, _i, _i, _i, _i]),
     "paged_attention_decode": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _z, _p]),
+    "paged_attention_decode_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]),
     "paged_attention_decode_partitions": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i,
                                                _p, _z, _p]),
     "paged_attention_decode_merge": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _p, _z, _p]),

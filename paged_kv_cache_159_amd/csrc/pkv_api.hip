@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "paged_kv.h"
 #include "pkv_device.h"
@@ -195,6 +196,35 @@ int device_accessible(const void* ptr, size_t bytes, const void** dev_ptr, bool*
   return PKV_OK;
 }
 
+// Scratch of paged_attention_decode_noalloc: the split-K partials of one
+// call, in a fixed device array (each GPU the library runs on holds its own
+// copy until the process ends). Host code never passes the array's name to a
+// kernel: it is a host-side stand-in, not a device address. The device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, or nullptr (with the
+// HIP error cleared) if it cannot be had.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +243,10 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PKV_ERR_SCRATCH:
+      return "the call needs more split-K scratch than paged_attention_decode_noalloc's fixed "
+             "device array holds (PKV_NOALLOC_SCRATCH_BYTES); use paged_attention_decode with a "
+             "workspace";
     case PKV_ERR_DATA:
       return "a data-dependent precondition does not hold (found by the PAGED_KV_DEBUG=1 "
              "device checks; nothing was launched)";
@@ -292,6 +326,37 @@ int paged_attention_decode(void* out, const void* query, const void* key_cache,
   rc = status_of(pkv::launch_decode_partitions(a, st));
   if (rc || a.num_parts <= 1) return rc;
   return status_of(pkv::launch_decode_merge(a, st));
+}
+
+int paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int num_seqs, int num_heads,
+                                   int head_dim, int num_blocks, int block_size,
+                                   int max_blocks_per_seq, float scale, int dtype, void* stream) {
+  // Host-side checks first (nothing touches the device before they pass).
+  int rc = check_layout(dtype, block_size, num_heads, head_dim, num_blocks);
+  if (rc) return rc;
+  int parts = 0;
+  size_t need = 0;
+  rc = check_decode(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, &parts, &need);
+  if (rc) return rc;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens))
+    return PKV_ERR_ALIGN;
+  void* ws = nullptr;
+  if (need) {
+    ws = scratch_on_current_device();
+    if (ws == nullptr) return PKV_ERR_LAUNCH;
+  }
+  return paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens,
+                                num_seqs, num_heads, head_dim, num_blocks, block_size,
+                                max_blocks_per_seq, scale, dtype, ws,
+                                (size_t)PKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t paged_attention_grouped_workspace_size(int num_seqs, int num_heads, int head_dim,

@@ -114,6 +114,23 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     return out
 
 
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, scale: float,
+                                   block_size: int | None = None) -> torch.Tensor:
+    """paged_attention_decode without a workspace: the library's fixed
+    per-device scratch array holds the partials, and nothing is allocated.
+    Calls overlapping on one GPU race on that array. Returns ``out``."""
+    dt, S, H, D, NB, MB, block_size = _decode_args(out, query, key_cache, value_cache,
+                                                   block_tables, context_lens, block_size)
+    rc = lib().paged_attention_decode_noalloc(out.data_ptr(), query.data_ptr(),
+                                              key_cache.data_ptr(), value_cache.data_ptr(),
+                                              block_tables.data_ptr(), context_lens.data_ptr(),
+                                              S, H, D, NB, block_size, MB, float(scale), dt,
+                                              _stream(out))
+    check("paged_attention_decode_noalloc", rc)
+    return out
+
+
 def grouped_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
                            max_blocks_per_seq: int, block_size: int = 16) -> int:
     return int(lib().paged_attention_grouped_workspace_size(num_seqs, num_heads, head_dim,
