@@ -771,7 +771,9 @@ def stats_summary(csv_path, w, grouped):
              f"{'grouped decode (shared-prefix MFMA units and tail partitions) + merge' if grouped else 'decode partition launch + merge launch'}; "
              "pool replicas rotated.", "",
              "Command (repo root, MI355X):", "", "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o s -- python -u bench.py "
+             "rocprofv3 --kernel-trace --stats --output-format csv -d "
+             f"{os.path.relpath(os.path.dirname(os.path.abspath(csv_path)), ROOT)} -o "
+             f"{os.path.basename(csv_path).split('_kernel_stats')[0]} -- python -u bench.py "
              f"--workload {w.index}{ung} --no-per-config --no-cpu-baseline", "```", "",
              f"Decode kernel source digest (bench.py `source_digest`): `{source_digest(grouped)}`.", "",
              "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
