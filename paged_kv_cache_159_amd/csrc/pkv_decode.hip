@@ -157,6 +157,63 @@ decode_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
   }
 }
 
+// The same merge for calls with at most kMergeSlotsFor128 partial slots per
+// (sequence, head), packed: one 256-thread workgroup per (sequence, block of
+// MH heads), thread (head, quad) merging four consecutive output elements
+// with 16-byte partial loads (MH = 8 at head size 128, 16 at 64). A
+// (sequence, head) in 2-wave workgroups took 4,096 workgroups at the
+// shared-prefix workload; this takes 512. Per element the arithmetic is the
+// single-chain pass above, so the outputs are the same bits.
+template <typename T, int D, bool GROUPED>
+__global__ void __launch_bounds__(256)
+decode_merge_packed_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
+                           const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens,
+                           int num_heads, int num_parts, int part_tokens,
+                           const int32_t* __restrict__ seq_tok0, int slot_base) {
+  using E = Elem<T>;
+  constexpr int QPH = D / 4;       // threads per head
+  constexpr int MH = 256 / QPH;    // heads per workgroup
+  const int H = num_heads;
+  const int hblocks = (H + MH - 1) / MH;
+  const int s = blockIdx.x / hblocks;
+  const int h = (blockIdx.x % hblocks) * MH + (int)threadIdx.x / QPH;
+  const int q = threadIdx.x % QPH;
+  const int ctx = context_lens[s];
+  int n0, n1;
+  if constexpr (GROUPED) {
+    constexpr int chunk_tokens = kSharedChunkTiles * kTileTokens;
+    const int st = seq_tok0[s];
+    n0 = (st + chunk_tokens - 1) / chunk_tokens;
+    n1 = (ctx - st + part_tokens - 1) / part_tokens;
+  } else {
+    n0 = (ctx + part_tokens - 1) / part_tokens;
+    n1 = 0;
+    if (n0 <= 1) return;  // written directly by the partition launch
+  }
+  if (h >= H) return;
+  const int n = n0 + n1;
+  const size_t base = ((size_t)s * H + h) * num_parts;
+  float M = -INFINITY, L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int i = 0; i < n; ++i) {
+    const size_t pi = base + (i < n0 ? i : slot_base + (i - n0));
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + pi * 2);
+    const float4 oi = *reinterpret_cast<const float4*>(ws_o + pi * D + 4 * q);
+    const float mn = fmaxf(M, ml.x);
+    const float a = fast_exp2(M - mn);
+    const float w = ml.y * fast_exp2(ml.x - mn);
+    L = L * a + w;
+    o.x = o.x * a + w * oi.x;
+    o.y = o.y * a + w * oi.y;
+    o.z = o.z * a + w * oi.z;
+    o.w = o.w * a + w * oi.w;
+    M = mn;
+  }
+  const uint2 r = make_uint2(E::pack2(o.x / L, o.y / L), E::pack2(o.z / L, o.w / L));
+  *reinterpret_cast<uint2*>(out + ((size_t)s * H + h) * D + 4 * q) = r;
+}
+
 int decode_partition_tokens(int max_blocks_per_seq, int block_size) {
   // 256 tokens while tables span at most 4096 tokens; 512 beyond, where the
   // grid is large anyway and fewer partials mean less merge traffic.
@@ -230,8 +287,24 @@ hipError_t merge_n(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D>
+hipError_t merge_packed(const DecodeArgs& a, hipStream_t st) {
+  constexpr int MH = 256 / (D / 4);
+  const unsigned grid = (unsigned)a.num_seqs * (unsigned)((a.num_heads + MH - 1) / MH);
+  if (a.ws_seq != nullptr) {
+    hipLaunchKernelGGL((decode_merge_packed_kernel<T, D, true>), dim3(grid), dim3(256), 0, st,
+                       static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens,
+                       a.num_heads, a.num_parts, a.part_tokens, a.ws_seq, a.slot_base);
+  } else {
+    hipLaunchKernelGGL((decode_merge_packed_kernel<T, D, false>), dim3(grid), dim3(256), 0, st,
+                       static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o, a.context_lens,
+                       a.num_heads, a.num_parts, a.part_tokens, nullptr, 0);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
 hipError_t merge_t(const DecodeArgs& a, hipStream_t st) {
-  return a.num_parts <= kMergeSlotsFor128 ? merge_n<T, D, 128>(a, st) : merge_n<T, D, 256>(a, st);
+  return a.num_parts <= kMergeSlotsFor128 ? merge_packed<T, D>(a, st) : merge_n<T, D, 256>(a, st);
 }
 }  // namespace
 

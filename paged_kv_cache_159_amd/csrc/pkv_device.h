@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace pkv {
@@ -122,6 +123,18 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
   x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
   return x;
+}
+
+// Maximum of x over the wave's 64 lanes, with the same DPP moves as the
+// prefix sum (a running maximum, read from lane 63).
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, kDppRowShr1, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, kDppRowShr2, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, kDppRowShr4, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, kDppRowShr8, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, kDppRowBcast15, 0xA, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, kDppRowBcast31, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(x, 63);
 }
 
 // Lane holding the (j + 1)-th set bit of the wave-uniform mask m (j <

@@ -270,14 +270,24 @@ decode_grouped_kernel(float* __restrict__ ws_ml, float* __restrict__ ws_o,
   constexpr int kLds = kSharedLdsBytes > partition_lds_bytes<D>() ? kSharedLdsBytes
                                                                   : partition_lds_bytes<D>();
   __shared__ __align__(16) uint8_t lds[kLds];
-  if ((int)blockIdx.x < tail_wgs) {
-    partition_body<T, D, PT, BS, true>(blockIdx.x, nullptr, ws_ml, ws_o, query, key_cache,
-                                   value_cache, block_tables, context_lens, num_seqs, num_heads,
-                                   max_blocks, num_parts, scale_log2, group_start, shared_blocks,
-                                   num_groups, chunk_slots, seq_tok0, lds);
+  // Grid order: the first tail partition of every (sequence, head group),
+  // then the shared-prefix units, then the later tail partitions (needed only
+  // by tails longer than PT tokens). Later partitions placed between the
+  // first ones and the shared units held the units back: at the shared-prefix
+  // workload (tails of 9-264 tokens) its 1,024 empty workgroups were
+  // dispatched first and the units started only at 37 of 66 us.
+  const int head_groups = (num_heads + shared_heads<D>() - 1) / shared_heads<D>();
+  const int first_wgs = num_seqs * ((num_heads + 64 / (D / 8) - 1) / (64 / (D / 8)));
+  const int shared_wgs = num_groups * chunk_slots * head_groups;
+  const int wg = blockIdx.x;
+  if (wg < first_wgs || wg >= first_wgs + shared_wgs) {
+    partition_body<T, D, PT, BS, true>(wg < first_wgs ? wg : wg - shared_wgs, nullptr, ws_ml,
+                                       ws_o, query, key_cache, value_cache, block_tables,
+                                       context_lens, num_seqs, num_heads, max_blocks, num_parts,
+                                       scale_log2, group_start, shared_blocks, num_groups,
+                                       chunk_slots, seq_tok0, lds);
   } else {
-    const int head_groups = (num_heads + shared_heads<D>() - 1) / shared_heads<D>();
-    const int u = blockIdx.x - tail_wgs;
+    const int u = wg - first_wgs;
     const int hg = u % head_groups;
     const int gc = u / head_groups;
     shared_unit<T, D, BS>(gc / chunk_slots, gc % chunk_slots, hg, ws_ml, ws_o, query, key_cache,

@@ -110,6 +110,53 @@ __device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
   return false;     // not reached: i < N
 }
 
+// Sequence of the grouped call's first-tail-partition slot sp (of num_seqs
+// slots): sequences by context length, longest first (kTailClasses classes
+// over the batch's range of lengths, sequences in order within a class), so
+// the tails that run last are the short ones. The tail is the context past
+// the group's shared prefix; ordering by the whole context is exact when
+// the groups share prefixes of one length and close otherwise. Returns -1
+// when the batch is too large to rank (the caller keeps slot order).
+constexpr int kTailClasses = 16;
+__device__ __forceinline__ int plan_tail_seq(int sp, int num_seqs,
+                                             const int32_t* __restrict__ context_lens) {
+  constexpr int KC = kPlanMaxSeqs / 64;
+  if (num_seqs > kPlanMaxSeqs) return -1;
+  const int lane = threadIdx.x & 63;
+  int cl[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int sq = 64 * k + lane;
+    cl[k] = (64 * k < num_seqs && sq < num_seqs) ? context_lens[sq] : -1;
+  }
+  int mx = INT_MIN, mn = INT_MAX;
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    if (64 * k < num_seqs) {   // wave-uniform
+      mx = max(mx, wave_max(cl[k]));
+      mn = min(mn, -wave_max(cl[k] < 0 ? INT_MIN + 1 : -cl[k]));
+    }
+  }
+  const int span = mx - mn + 1;
+  int cls[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k)
+    cls[k] = cl[k] < 0 ? -1 : (int)(((int64_t)(mx - cl[k]) * kTailClasses) / span);
+  int j = sp;
+#pragma unroll 1
+  for (int c = 0; c < kTailClasses; ++c) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      if (64 * k >= num_seqs) break;
+      const uint64_t m = __ballot(cls[k] == c);
+      const int cnt = __popcll(m);
+      if (j < cnt) return 64 * k + nth_set_lane(m, j);
+      j -= cnt;
+    }
+  }
+  return -1;   // not reached: sp < num_seqs
+}
+
 // Grid slots of the plain launch whose items plan_item orders (above this the
 // grid keeps its plain order, partition-major): slot arithmetic stays in 32
 // bits.
@@ -151,6 +198,12 @@ __device__ __forceinline__ void partition_body(
   const int sp = wg / groups;
   int s = sp % num_seqs;
   int p = sp / num_seqs;
+  if constexpr (TAIL) {
+    if (p == 0) {   // first tail partitions: longest contexts first
+      const int ts = plan_tail_seq(s, num_seqs, context_lens);
+      if (ts >= 0 && ts < num_seqs) s = __builtin_amdgcn_readfirstlane(ts);
+    }
+  }
   if constexpr (!TAIL) {
     if (plan_fits(num_seqs, num_parts)) {
       int ps = 0, pp = 0;
@@ -163,6 +216,23 @@ __device__ __forceinline__ void partition_body(
       p = __builtin_amdgcn_readfirstlane(pp);
     }
   }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hl = lane / LPR;          // head within the group
+  const int c = lane % LPR;           // 8-element column chunk
+  const int h = g * HG + hl;
+  const bool head_ok = h < H;
+  const int hr = head_ok ? h : 0;     // lanes past the last head read head 0 and are ignored
+
+  // Loads that depend only on (s, g) go out first, together: the query, the
+  // context length and (tails) the group lookup and the first 64 table
+  // entries. A tail's first block is known only after the group lookup, so
+  // its entries are read from this speculative copy when they lie in it,
+  // which saves a dependent memory round trip per workgroup.
+  const uint4 qv = *reinterpret_cast<const uint4*>(query + ((size_t)s * H + hr) * D + c * 8);
+  int32_t table_spec = 0;
+  if constexpr (TAIL)
+    table_spec = lane < max_blocks ? block_tables[(size_t)s * max_blocks + lane] : 0;
   const int ctx = context_lens[s];
   int tok0 = 0;   // first token this launch covers for sequence s
   if constexpr (TAIL)
@@ -176,21 +246,19 @@ __device__ __forceinline__ void partition_body(
   // tok0 (a multiple of 16) and PT are multiples of the tile and the block
   const int nsteps = (tok_end - tok_begin + STEP - 1) / STEP;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int hl = lane / LPR;          // head within the group
-  const int c = lane % LPR;           // 8-element column chunk
-  const int h = g * HG + hl;
-  const bool head_ok = h < H;
-  const int hr = head_ok ? h : 0;     // lanes past the last head read head 0 and are ignored
-
-  const uint4 qv = *reinterpret_cast<const uint4*>(query + ((size_t)s * H + hr) * D + c * 8);
   // The partition's table entries, one per lane (at most 64), loaded once;
-  // the loop reads them with v_readlane (no memory latency per step).
+  // the loop reads them with v_readlane (no memory latency per step): entry
+  // j sits in lane j - tbase of table_lane.
   const uint32_t blk0 = (uint32_t)tok_begin / BS;
   const int nblk = (tok_end - tok_begin + BS - 1) / BS;
-  const int32_t table_lane =
-      lane < nblk ? block_tables[(size_t)s * max_blocks + blk0 + lane] : 0;
+  int32_t table_lane;
+  uint32_t tbase = blk0;              // table entry held by lane 0
+  if (TAIL && blk0 + nblk <= 64) {
+    table_lane = table_spec;
+    tbase = 0;
+  } else {
+    table_lane = lane < nblk ? block_tables[(size_t)s * max_blocks + blk0 + lane] : 0;
+  }
   const uint32_t kv_dim = (uint32_t)H * D;
   const size_t blk_bytes = (size_t)BS * kv_dim * sizeof(uint16_t);
   const uint32_t row_bytes = kv_dim * (uint32_t)sizeof(uint16_t);
@@ -217,7 +285,7 @@ __device__ __forceinline__ void partition_body(
       // With one tile per step at block sizes >= 16, the tile sits in the
       // block of tb.
       const uint32_t bi =
-          ((kTilesPerStep == 1 && BS >= kTileTokens) ? (uint32_t)tb : te) / BS - blk0;
+          ((kTilesPerStep == 1 && BS >= kTileTokens) ? (uint32_t)tb : te) / BS - tbase;
       const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(table_lane, bi);
       const uint32_t off = (te % BS) * row_bytes + col_bytes;
       // Non-temporal V loads: a row read once per launch should not displace
