@@ -248,7 +248,7 @@ __device__ __forceinline__ void shared_unit(
 
 // The grouped call's main launch: workgroups [0, tail_wgs) run tail partitions
 // exactly as the partition kernel does in TAIL mode; the rest run shared-prefix
-// units (head fastest, then chunk, then group). Both kinds share one grid, so
+// units (head fastest, then group, then chunk). Both kinds share one grid, so
 // they overlap on the machine; the tails (several blocks per sequence and head
 // group) are dispatched first and the short shared units fill in behind them.
 template <typename T, int D, int PT, int BS>
@@ -287,10 +287,12 @@ decode_grouped_kernel(float* __restrict__ ws_ml, float* __restrict__ ws_o,
                                        scale_log2, group_start, shared_blocks, num_groups,
                                        chunk_slots, seq_tok0, lds);
   } else {
+    // Chunk-major: every group's first chunk, then every group's second, ...
+    // so the short last chunks and the empty chunk slots come last.
     const int u = wg - first_wgs;
     const int hg = u % head_groups;
     const int gc = u / head_groups;
-    shared_unit<T, D, BS>(gc / chunk_slots, gc % chunk_slots, hg, ws_ml, ws_o, query, key_cache,
+    shared_unit<T, D, BS>(gc % num_groups, gc / num_groups, hg, ws_ml, ws_o, query, key_cache,
                       value_cache, block_tables, group_start, shared_blocks, num_heads,
                       max_blocks, num_parts, scale_log2, lds);
   }

@@ -216,6 +216,12 @@ __device__ __forceinline__ void partition_body(
       p = __builtin_amdgcn_readfirstlane(pp);
     }
   }
+  if constexpr (TAIL) {
+    // A later tail partition starts at least p * PT tokens in: past the
+    // context it has nothing to do, known from the context length alone
+    // (most of these slots are empty: tails are usually shorter than PT).
+    if (p > 0 && p * PT >= context_lens[s]) return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane / LPR;          // head within the group
