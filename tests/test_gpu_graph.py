@@ -142,3 +142,47 @@ def test_graph_prefill_replays():
         call(out_e)
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), f"replay {r}"
+
+
+def test_graph_staged_swap_replays():
+    """swap_blocks_staged (DMA of runs of host blocks into a device staging
+    buffer, then scatter launches whose destination ids travel in their
+    kernel arguments) captured once and replayed with new host contents; a
+    staging buffer of 5 slots makes the 12 pairs run as 3 chunks."""
+    say("swap_blocks_staged (host -> device) in a graph, 4 replays")
+    pkv = _pkv()
+    w = make_decode_case([300, 1000, 17, 513], 4, 128, "f16", seed=51, max_blocks=64)
+    dw = upload(w)
+    nb = dw.key_cache.shape[0]
+    shape = (24,) + tuple(dw.key_cache.shape[1:])
+    hk = torch.empty(shape, dtype=dw.key_cache.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=dw.key_cache.dtype, pin_memory=True)
+    rng = np.random.default_rng(5)
+    src = np.array([0, 1, 2, 3, 7, 8, 10, 15, 16, 17, 18, 20])
+    dst = rng.choice(nb, len(src), replace=False)
+    mapping = torch.from_numpy(np.stack([src, dst], axis=1).astype(np.int32))
+    block_bytes = hk[0].numel() * hk.element_size()
+    staging = torch.empty(5 * 2 * block_bytes, dtype=torch.uint8, device="cuda")
+    kc_g, vc_g = dw.key_cache.clone(), dw.value_cache.clone()
+    kc_e, vc_e = dw.key_cache.clone(), dw.value_cache.clone()
+
+    def fill(r):
+        g_ = torch.Generator().manual_seed(100 + r)
+        hk.view(torch.int16).copy_(torch.randint(-30000, 30000, shape, generator=g_, dtype=torch.int16))
+        hv.view(torch.int16).copy_(torch.randint(-30000, 30000, shape, generator=g_, dtype=torch.int16))
+
+    fill(0)
+    g = capture(lambda: pkv.swap_blocks(hk, hv, kc_g, vc_g, mapping, method="staged",
+                                        staging=staging))
+    for r in range(REPLAYS):
+        fill(r + 1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        pkv.swap_blocks(hk, hv, kc_e, vc_e, mapping, method="staged", staging=staging)
+        torch.cuda.synchronize()
+        assert torch.equal(kc_g.view(torch.int16), kc_e.view(torch.int16)), f"replay {r}: keys"
+        assert torch.equal(vc_g.view(torch.int16), vc_e.view(torch.int16)), f"replay {r}: values"
+        moved = torch.from_numpy(dst).long().cuda()
+        assert torch.equal(kc_g[moved].cpu().view(torch.int16),
+                           hk[torch.from_numpy(src).long()].view(torch.int16)), f"replay {r}"
