@@ -102,8 +102,11 @@ const char* pkv_status_string(int status);
 /*
  * Workspace bytes paged_attention_decode needs for these sizes: fp32 partial
  * results (running max, exponent sum and a head_dim vector) of every context
- * partition of every (sequence, head). A partition is 256 tokens when
- * max_blocks_per_seq*block_size <= 4096, else 512 tokens. Returns 0 when no
+ * partition of every (sequence, head). A partition is 512 tokens when
+ * max_blocks_per_seq*block_size > 4096, or when num_seqs * ceil(num_heads /
+ * G) * ceil(max_blocks_per_seq*block_size / 256) >= 8192 (G = 4 heads at
+ * head_dim 128, 8 at 64: the heads one workgroup covers), else 256 tokens.
+ * Returns 0 when no
  * sequence can span more than one partition or when the arguments are
  * invalid.
  */
@@ -118,8 +121,8 @@ size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
  *     out[s][h] = sum_t softmax(x)_t * V_t
  * where K_t and V_t are token t's rows of head h, found through block_tables[s].
  * Accumulation is fp32; the output is rounded to nearest-even into `dtype`.
- * Contexts are split into partitions of 256 tokens (512 when
- * max_blocks_per_seq*block_size > 4096) whose partial results are merged by
+ * Contexts are split into partitions of 256 or 512 tokens (the rule at
+ * paged_attention_workspace_size) whose partial results are merged by
  * log-sum-exp; the reduction order depends only
  * on logical token positions, so relabelling physical blocks leaves `out`
  * bit-identical.

@@ -33,9 +33,11 @@ int check_layout(int dtype, int block_size, int num_heads, int head_dim, int num
   return PKV_OK;
 }
 
-int num_partitions(int max_blocks_per_seq, int block_size) {
+int num_partitions(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
+                   int block_size) {
   const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
-  const int pt = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
+  const int pt = pkv::decode_partition_tokens(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                              block_size);
   return (int)((tokens + pt - 1) / pt);
 }
 
@@ -44,7 +46,7 @@ int check_decode(int num_seqs, int num_heads, int head_dim, int block_size,
                  int max_blocks_per_seq, int* parts, size_t* need) {
   if (num_seqs < 0 || max_blocks_per_seq < 1) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxGrid) return PKV_ERR_SHAPE;
-  *parts = num_partitions(max_blocks_per_seq, block_size);
+  *parts = num_partitions(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size);
   if ((int64_t)num_seqs * num_heads * (*parts) > kMaxGrid) return PKV_ERR_SHAPE;
   *need = (*parts > 1) ? pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, *parts) : 0;
   return PKV_OK;
@@ -113,7 +115,8 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->max_blocks_per_seq = max_blocks_per_seq;
   a->block_size = block_size;
   a->num_parts = parts;
-  a->part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
+  a->part_tokens = pkv::decode_partition_tokens(num_seqs, num_heads, head_dim,
+                                                  max_blocks_per_seq, block_size);
   a->scale = scale;
   a->dtype = dtype;
   a->tail_parts = parts;
@@ -305,7 +308,8 @@ int paged_attention_decode_merge(void* out, const int32_t* context_lens, int num
   a.block_size = block_size;
   a.num_parts = parts;
   a.tail_parts = parts;
-  a.part_tokens = pkv::decode_partition_tokens(max_blocks_per_seq, block_size);
+  a.part_tokens = pkv::decode_partition_tokens(num_seqs, num_heads, head_dim,
+                                                  max_blocks_per_seq, block_size);
   a.dtype = dtype;
   pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a.ws_ml, &a.ws_o);
   return status_of(pkv::launch_decode_merge(a, static_cast<hipStream_t>(stream)));

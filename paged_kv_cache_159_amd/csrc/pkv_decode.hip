@@ -214,11 +214,21 @@ decode_merge_packed_kernel(uint16_t* __restrict__ out, const float* __restrict__
   *reinterpret_cast<uint2*>(out + ((size_t)s * H + h) * D + 4 * q) = r;
 }
 
-int decode_partition_tokens(int max_blocks_per_seq, int block_size) {
-  // 256 tokens while tables span at most 4096 tokens; 512 beyond, where the
-  // grid is large anyway and fewer partials mean less merge traffic.
+int decode_partition_tokens(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
+                            int block_size) {
+  // 512 tokens when tables span more than 4096 tokens, or when 256-token
+  // partitions would make a grid of 8192 or more (sequence, partition, head
+  // group) slots; 256 otherwise. Measured on MI355X (32 heads x 128, fp16,
+  // decode call, 256 -> 512): 64 sequences of U[128, 2048] 167.1 -> 170.5 us
+  // and 64 of Exp(512) 89.2 -> 94.6 us (4096 slots: 256 stays), but 128 of
+  // U[128, 2048] 368.5 -> 364.4, 256 of Exp(512) 358.1 -> 350.4 and 256 of
+  // U[128, 2048] 694.0 -> 684.5 (8192 and 16384 slots): large batches have
+  // items enough to balance, and fewer partials to write and merge.
   const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
-  return tokens <= 4096 ? 256 : 512;
+  if (tokens > 4096) return 512;
+  const int64_t head_groups = (num_heads + 64 / (head_dim / 8) - 1) / (64 / (head_dim / 8));
+  const int64_t slots = (int64_t)num_seqs * head_groups * ((tokens + 255) / 256);
+  return slots >= kLargeGridSlots ? 512 : 256;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int num_parts) {

@@ -42,8 +42,12 @@ struct DecodeArgs {
                         // written by the main launch, read by the merge
 };
 
-// Tokens per context partition for these sizes (256 or 512).
-int decode_partition_tokens(int max_blocks_per_seq, int block_size);
+// Tokens per context partition for these sizes (256 or 512): 512 for tables
+// of more than 4096 tokens or grids of kLargeGridSlots or more 256-token
+// (sequence, partition, head group) slots.
+constexpr int64_t kLargeGridSlots = 8192;
+int decode_partition_tokens(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
+                            int block_size);
 
 // Workspace layout shared by the two decode launches.
 size_t decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int num_parts);

@@ -49,10 +49,13 @@ def test_version_and_status_strings(L):
 
 
 def _expected_workspace(S, H, D, MB, bs=16):
-    """The documented rule: 256-token partitions up to 4096 tokens per table,
-    512 beyond; (max, sum) pairs padded to 256 bytes, then fp32 vectors."""
+    """The documented rule: 512-token partitions beyond 4096 tokens per table
+    or from 8192 slots of 256 tokens (sequences x head groups x partitions;
+    4 heads per group at head_dim 128, 8 at 64), else 256; (max, sum) pairs
+    padded to 256 bytes, then fp32 vectors."""
     tokens = MB * bs
-    pt = 256 if tokens <= 4096 else 512
+    groups = -(-H // (4 if D == 128 else 8))
+    pt = 256 if tokens <= 4096 and S * groups * -(-tokens // 256) < 8192 else 512
     P = -(-tokens // pt)
     if P <= 1:
         return 0
@@ -66,9 +69,14 @@ def test_workspace_size(L):
                         (64, 32, 128, 257), (8, 32, 128, 2048), (3, 5, 64, 1000)):
         assert L.paged_attention_workspace_size(S, H, D, MB, 16) == _expected_workspace(S, H, D, MB)
     assert _expected_workspace(64, 32, 128, 128) == 64 * 32 * 8 * 8 + 64 * 32 * 8 * 512
+    # 128 sequences x 8 head groups x 8 slots = 8192: 512-token partitions
+    assert _expected_workspace(128, 32, 128, 128) == 128 * 32 * 4 * 8 + 128 * 32 * 4 * 512
+    assert L.paged_attention_workspace_size(128, 32, 128, 128, 16) == 128 * 32 * 4 * 520
+    assert L.paged_attention_workspace_size(127, 32, 128, 128, 16) == 127 * 32 * 8 * 520
     assert L.paged_attention_workspace_size(8, 32, 96, 2048, 16) == 0  # invalid -> 0
     for bs in (8, 32):                                                   # the other block sizes
-        for S, H, D, MB in ((4, 4, 64, 32), (4, 4, 64, 33), (64, 32, 128, 256), (8, 32, 128, 4096)):
+        for S, H, D, MB in ((4, 4, 64, 32), (4, 4, 64, 33), (64, 32, 128, 256), (8, 32, 128, 4096),
+                            (256, 32, 64, 64), (300, 6, 128, 100)):
             assert L.paged_attention_workspace_size(S, H, D, MB, bs) == \
                 _expected_workspace(S, H, D, MB, bs), (bs, S, H, D, MB)
     for bs in (0, 4, 12, 24, 64, -16):
