@@ -33,17 +33,23 @@ constexpr int partition_lds_bytes() {
 // fp16): 64 sequences of U[128, 2048] tokens 169.7 -> 164.3 us, 64 of
 // Exp(512) 87.5 -> 83.5, 128 of U[128, 2048] 372.0 -> 361.5, 256 of
 // U[128, 2048] 690.4 -> 682.5, 256 of Exp(512) and 8 x 32K unchanged
-// (351.7, 633.7 -> 629.0).
+// (351.7, 633.7 -> 629.0). The plan is not free: per-workgroup timestamps put
+// ~1.3 us between a workgroup's start and its first item load (the context
+// lengths' load, then a dependent chain of ~150 instructions issued by all
+// 8 waves), which loses where items are short, e.g. 8 beams per prompt
+// reading shared blocks (97 -> 108 us); there the longest-first order has
+// little to balance.
 constexpr int kPlanMaxSeqs = 256;   // context lengths held in registers (4 per lane)
 constexpr int kRemClasses = 8;
 
-// Item of grid slot sp (of num_seqs * num_parts slots): sequence s and
-// partition p; false for a slot with no item. Computed by each wave from the
-// context lengths (one load per lane and 64 sequences), wave-uniform.
+// Item of grid slot sp (of num_seqs * num_parts slots): sequence s, partition
+// p and the sequence's context length ctx (read from the registers the plan
+// already holds); false for a slot with no item. Computed by each wave from
+// the context lengths (one load per lane and 64 sequences), wave-uniform.
 template <int PT>
 __device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
                                           const int32_t* __restrict__ context_lens, int& s,
-                                          int& p) {
+                                          int& p, int& ctx) {
   constexpr int KC = kPlanMaxSeqs / 64;
   const int lane = threadIdx.x & 63;
   int cl[KC];
@@ -56,8 +62,8 @@ __device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
   int F = 0, R = 0;
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
-    nf[k] = cl[k] / PT;
-    const int r = cl[k] % PT;
+    nf[k] = (int)((uint32_t)cl[k] / PT);
+    const int r = (int)((uint32_t)cl[k] % PT);
     cls[k] = r ? (r * kRemClasses + PT - 1) / PT : 0;   // 1 .. kRemClasses
     incl[k] = 0;
     tot[k] = 0;
@@ -84,6 +90,7 @@ __device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
         const int ln = __ffsll((unsigned long long)__ballot(incl[k] > j)) - 1;
         s = 64 * k + ln;
         p = j - __builtin_amdgcn_readlane(incl[k] - nf[k], ln);
+        ctx = __builtin_amdgcn_readlane(cl[k], ln);
         return true;
       }
       j -= tot[k];
@@ -102,6 +109,7 @@ __device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
         const int ln = nth_set_lane(m, j);
         s = 64 * k + ln;
         p = __builtin_amdgcn_readlane(nf[k], ln);
+        ctx = __builtin_amdgcn_readlane(cl[k], ln);
         return true;
       }
       j -= cnt;
@@ -204,16 +212,18 @@ __device__ __forceinline__ void partition_body(
       if (ts >= 0 && ts < num_seqs) s = __builtin_amdgcn_readfirstlane(ts);
     }
   }
+  int planned_ctx = -1;   // the item's context length when the plan gave it
   if constexpr (!TAIL) {
     if (plan_fits(num_seqs, num_parts)) {
-      int ps = 0, pp = 0;
-      const bool real = plan_item<PT>(sp, num_seqs, num_parts, context_lens, ps, pp);
+      int ps = 0, pp = 0, pc = 0;
+      const bool real = plan_item<PT>(sp, num_seqs, num_parts, context_lens, ps, pp, pc);
       // an item outside the grid's (sequence, partition) range is never
       // produced; the bound keeps every later index inside the arrays anyway
       if (!real || (unsigned)ps >= (unsigned)num_seqs || (unsigned)pp >= (unsigned)num_parts)
         return;
       s = __builtin_amdgcn_readfirstlane(ps);
       p = __builtin_amdgcn_readfirstlane(pp);
+      planned_ctx = __builtin_amdgcn_readfirstlane(pc);
     }
   }
   if constexpr (TAIL) {
@@ -230,16 +240,24 @@ __device__ __forceinline__ void partition_body(
   const bool head_ok = h < H;
   const int hr = head_ok ? h : 0;     // lanes past the last head read head 0 and are ignored
 
-  // Loads that depend only on (s, g) go out first, together: the query, the
-  // context length and (tails) the group lookup and the first 64 table
-  // entries. A tail's first block is known only after the group lookup, so
-  // its entries are read from this speculative copy when they lie in it,
-  // which saves a dependent memory round trip per workgroup.
+  // Loads that depend only on (s, p, g) go out first, together: the query,
+  // the context length (unless the item plan already holds it), the
+  // partition's table entries (plain partitions) or the first 64 entries and
+  // the group lookup (tails). A tail's first block is known only after the
+  // group lookup, so its entries are read from this speculative copy when
+  // they lie in it. Either way the table load does not wait for another
+  // memory round trip.
   const uint4 qv = *reinterpret_cast<const uint4*>(query + ((size_t)s * H + hr) * D + c * 8);
   int32_t table_spec = 0;
-  if constexpr (TAIL)
+  if constexpr (TAIL) {
     table_spec = lane < max_blocks ? block_tables[(size_t)s * max_blocks + lane] : 0;
-  const int ctx = context_lens[s];
+  } else {
+    // The partition's PT / BS entries (those inside the table): a superset of
+    // the ones its tokens use, loaded without waiting for the context length.
+    const int e = p * (PT / BS) + lane;
+    table_spec = (lane < PT / BS && e < max_blocks) ? block_tables[(size_t)s * max_blocks + e] : 0;
+  }
+  const int ctx = planned_ctx >= 0 ? planned_ctx : context_lens[s];
   int tok0 = 0;   // first token this launch covers for sequence s
   if constexpr (TAIL)
     tok0 = shared_prefix_tokens(group_shared_blocks(s, group_start, shared_blocks, num_groups), BS);
@@ -259,7 +277,9 @@ __device__ __forceinline__ void partition_body(
   const int nblk = (tok_end - tok_begin + BS - 1) / BS;
   int32_t table_lane;
   uint32_t tbase = blk0;              // table entry held by lane 0
-  if (TAIL && blk0 + nblk <= 64) {
+  if constexpr (!TAIL) {
+    table_lane = table_spec;       // entry blk0 + j in lane j
+  } else if (blk0 + nblk <= 64) {
     table_lane = table_spec;
     tbase = 0;
   } else {
