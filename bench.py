@@ -464,8 +464,17 @@ def prefill_bench(args, dev):
         f = lambda: pkv.paged_attention_prefill(dw.out, dw.query, dw.key_cache, dw.value_cache,
                                                 dw.block_tables, dw.context_lens, dw.query_start,
                                                 w.scale, max_query_len=mq)
-        for _ in range(3):
+        # Warm up for at least 0.3 s of back-to-back calls: building the
+        # workload leaves the GPU idle for seconds, and the clock takes longer
+        # than a few calls to come back up under this MFMA load (with 3 calls
+        # of warm-up the timed calls ran ~14% slower than in steady state).
+        t_end = time.perf_counter() + 0.3
+        n = 0
+        while n < 3 or time.perf_counter() < t_end:
             f()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         evs = []
         for _ in range(max(5, min(args.steps, 30))):
@@ -476,10 +485,12 @@ def prefill_bench(args, dev):
             e1.record()
             evs.append((e0, e1))
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        times = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        us = float(np.median(times))
         fl = prefill_flops(w)
         tf = fl / (us * 1e-6) / 1e12
-        res[name] = {"kernel_us": round(us, 1), "flops": fl, "tflops": round(tf, 1),
+        res[name] = {"kernel_us": round(us, 1), "kernel_us_mean": round(float(np.mean(times)), 1),
+                     "warmup_calls": n, "flops": fl, "tflops": round(tf, 1),
                      "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS[args.dtype], 4),
                      "tokens": int(sum(chunks)), "tokens_per_s": round(sum(chunks) / (us * 1e-6), 1),
                      "chunks": chunks, "cached": cached}

@@ -17,8 +17,8 @@
 // are dispatched last-first (the causal work of a tile grows with its
 // position). Keys are staged through LDS 64 at a time, gathered row by row
 // through the block table (any block size); one barrier per stage. At head
-// size 128 the rows go from global memory straight into a ring of three LDS
-// buffers (global_load_lds_dwordx4; the next two stages arrive while the
+// size 128 the rows go from global memory straight into a ring of four LDS
+// buffers (global_load_lds_dwordx4; the next three stages arrive while the
 // waves compute on the current one), K and V both row-major with
 // XOR-swizzled 16-byte pieces, and P.V reads its V^T operands with gfx950's
 // transposing LDS read (ds_read_b64_tr_b16). Other head sizes stage through
@@ -105,6 +105,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   constexpr int PER_THREAD = PIECES / THREADS;
   static_assert(PIECES % THREADS == 0, "whole pieces per thread");
   constexpr int NBUF = 2;   // register-staged stages alternate between two buffers
+  constexpr bool kPrio = !std::is_same<T, BF16>::value;   // wave priorities (below)
   // Direct staging (head size 128): K and V rows go from global memory
   // straight into LDS (one 16-byte load per lane, lane l landing at the
   // instruction's base + 16 l), unpadded 256-byte rows with XOR-swizzled
@@ -114,12 +115,15 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   constexpr bool kDirect = D == 128;
   constexpr int kDirectRow = 2 * D;                       // 256 bytes
   constexpr int kDirectStage = 2 * kPrefillKeys * kDirectRow;   // K rows, then V rows
-  // A ring of three stage buffers: the loads of stages st + 1 and st + 2 fly
+  // A ring of four stage buffers: the loads of stages st + 1 .. st + 3 fly
   // while stage st is computed (the kernel's registers allow one workgroup
-  // per CU, so its LDS can take 96 KiB).
+  // per CU, so its LDS can take 128 KiB). Three buffers measured 1-3% slower
+  // (fp16 chunks 373.0 vs 361.0 us, bf16 whole prompts 685.8 vs 665.2 us with
+  // the priorities below).
   __shared__ __align__(16) uint8_t s_d0[kDirect ? kDirectStage : 16];
   __shared__ __align__(16) uint8_t s_d1[kDirect ? kDirectStage : 16];
   __shared__ __align__(16) uint8_t s_d2[kDirect ? kDirectStage : 16];
+  __shared__ __align__(16) uint8_t s_d3[kDirect ? kDirectStage : 16];
   __shared__ __align__(16) uint8_t s_kbuf[kDirect ? 1 : NBUF][kDirect ? 16 : kPrefillKeys * KROW];
   constexpr int VTROW = kVtRow;
   __shared__ __align__(16) uint8_t s_vtbuf[kDirect ? 1 : NBUF][kDirect ? 16 : D * VTROW];
@@ -258,8 +262,10 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as the
   // builtin so the compiler's own wait placement sees it.
   constexpr int kWaitVmcnt0 = 0x0F70;
-  // s_waitcnt vmcnt(4): all but one stage's four loads of this wave done.
+  // s_waitcnt vmcnt(4) / vmcnt(8): all but the last one / two stages' four
+  // loads of this wave done.
   constexpr int kWaitVmcnt4 = 0x0F74;
+  constexpr int kWaitVmcnt8 = 0x0F78;
   if constexpr (kDirect) {
     // Stage 0 and the query rows first (waited for here, so the compiler
     // knows the query registers are ready and puts no wait of its own in
@@ -267,6 +273,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     issue_stage(0, s_d0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (nstages > 1) issue_stage(1, s_d1);
+    if (nstages > 2) issue_stage(2, s_d2);
     __syncthreads();
   } else {
     load_stage(0);
@@ -278,13 +285,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint8_t* s_k;
     const uint8_t* s_vt;
     if constexpr (kDirect) {
-      const int b = st % 3;
-      uint8_t* cur = b == 0 ? s_d0 : (b == 1 ? s_d1 : s_d2);
-      uint8_t* nxt2 = b == 0 ? s_d2 : (b == 1 ? s_d0 : s_d1);
-      // Stage st + 2's loads go to the buffer stage st - 1 used (every wave
+      const int b = st & 3;
+      uint8_t* cur = b == 0 ? s_d0 : (b == 1 ? s_d1 : (b == 2 ? s_d2 : s_d3));
+      uint8_t* nxt3 = b == 0 ? s_d3 : (b == 1 ? s_d0 : (b == 2 ? s_d1 : s_d2));
+      // Stage st + 3's loads go to the buffer stage st - 1 used (every wave
       // finished reading it before the barrier that ended stage st - 1) and
-      // fly during this stage's and the next one's math.
-      if (st + 2 < nstages) issue_stage(st + 2, nxt2);
+      // fly during the math of this stage and the next two.
+      if (st + 3 < nstages) issue_stage(st + 3, nxt3);
       s_k = cur;
       s_vt = cur + kPrefillKeys * kDirectRow;
     } else {
@@ -327,10 +334,12 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
                                                     (32 * i + 8 * grp) * 2);
           }
         }
-        // Wave priority: the softmax (a chain of dependent VALU work) runs
-        // at priority 1 and the MFMA blocks at 0, so on a SIMD the wave in
-        // its softmax wins issue slots while the other wave's MFMAs run.
-        __builtin_amdgcn_s_setprio(0);
+        // Wave priority (fp16): the softmax (a chain of dependent VALU work)
+        // runs at priority 1 and the MFMA blocks at 0, so on a SIMD the wave
+        // in its softmax wins issue slots while the other wave's MFMAs run.
+        // bf16, whose split P doubles the P.V MFMAs, ran 3-4% faster without
+        // the priorities; fp16 1-2% slower.
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
         f4_t sa[QW], sb[QW];
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
@@ -344,7 +353,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         }
         constexpr bool kSplit = std::is_same<T, BF16>::value;
         uint4 bhi[QW], blo[QW];
-        __builtin_amdgcn_s_setprio(1);
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
         // Exponents against the current reference: y = s * scale - m in the
         // log2 domain, one FMA per score (masked keys -inf). The reference
         // stays unless some score of the step exceeds it by more than
@@ -398,7 +407,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
         // accumulators in place (a rescale joining a shared P.V block made
         // the compiler copy all 64 accumulator registers every step).
         auto pv_block = [&]() {
-          __builtin_amdgcn_s_setprio(0);
+          if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             const int d = 16 * c + col;
@@ -485,7 +494,7 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
           weights();
           pv_block();
         }
-        __builtin_amdgcn_s_setprio(1);
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
       };
       if (kbase + 31 > first + wrow0)
         step(std::true_type{});
@@ -495,9 +504,11 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     }
     if constexpr (kDirect) {
       // Stage st + 1 has landed once this wave's loads up to it are done
-      // (only stage st + 2's four may still fly: loads complete in order) and
-      // every wave has passed the barrier.
-      if (st + 2 < nstages)
+      // (only those of stages st + 2 and st + 3 may still fly: loads complete
+      // in order) and every wave has passed the barrier.
+      if (st + 3 < nstages)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt8);
+      else if (st + 2 < nstages)
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
       else
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
