@@ -227,7 +227,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
   auto issue_stage = [&](int st, uint8_t* buf) {
     // Table lookups and addresses of all four loads first, then the loads
     // back to back (a lookup between them would wait for the loads before it).
-    const uint16_t* src[4];
+    // Each load takes a wave-uniform 64-bit base (the block's first row of
+    // this head, in SGPRs) and a 32-bit per-lane byte offset: against a
+    // 64-bit address per lane this frees VGPRs and VALU address arithmetic
+    // (fp16 whole prompts 537.4 -> 525.7 us, chunks 379.8 -> 359.7 us; bf16
+    // within 1%).
+    const uint16_t* sbase[4];
+    uint32_t voff[4];
     uint32_t lds_base[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -240,23 +246,23 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       // table entry is a scalar load (not a vector load, whose wait would
       // also wait for the stage loads in flight).
       const int32_t phys = bt[min(st * kPrefillKeys + r0, nkeys - 1) / BS];
-      const size_t slot = (size_t)phys * BS + (kpos % BS);
-      src[j] = (tensor ? value_cache : key_cache) + slot * kv_dim + (size_t)h * D + piece * 8;
+      sbase[j] = (tensor ? value_cache : key_cache) + (size_t)phys * BS * kv_dim + (size_t)h * D;
+      voff[j] = (uint32_t)(((kpos % BS) * kv_dim + piece * 8) * sizeof(uint16_t));
       lds_base[j] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
           buf + tensor * kPrefillKeys * kDirectRow + r0 * kDirectRow);
     }
     // global_load_lds_dwordx4 with the wave-uniform LDS base in M0. Written
     // as inline asm so the compiler does not treat the loads as LDS writes
-    // that every later LDS read must wait for: the loads go to the buffer the
+    // that every later LDS read must wait for: the loads go to a buffer the
     // current stage does not read, and the stage loop waits for them itself
-    // (s_waitcnt vmcnt(0), then a barrier) before that buffer is read. Loads
+    // (s_waitcnt vmcnt, then a barrier) before that buffer is read. Loads
     // unknown to the compiler only make its own vmcnt waits more
     // conservative (vector loads complete in order). m0 (the DMA's LDS
     // address) is set in the same statement and used by nothing else here.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :: "s"(lds_base[j]), "v"(src[j]) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(lds_base[j]), "v"(voff[j]), "s"(sbase[j]) : "memory", "m0");
   };
 
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as the
