@@ -125,6 +125,9 @@ __device__ __forceinline__ void shared_unit(
   };
   const uint32_t k_elem = piece_elems((lane & 31) ^ (lrow & 15));
   const uint32_t v_elem = piece_elems((lane & 31) ^ (2 * (lrow & 7)));
+  // byte offsets of this lane's piece from its tile row pair's first row
+  const uint32_t k_off = ((uint32_t)(lane >> 5) * (uint32_t)kv_dim + k_elem) * (uint32_t)sizeof(uint16_t);
+  const uint32_t v_off = ((uint32_t)(lane >> 5) * (uint32_t)kv_dim + v_elem) * (uint32_t)sizeof(uint16_t);
   auto lds_addr = [](const uint8_t* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p);
   };
@@ -137,13 +140,13 @@ __device__ __forceinline__ void shared_unit(
   auto issue_tile = [&](int b, uint8_t* buf) {
     const int tw = t0_chunk + b * kTileTokens + 2 * wave;   // wave-uniform
     const int32_t phys = __builtin_amdgcn_readlane(table_lane, tw / BS - blk0);
-    const size_t row = ((size_t)phys * BS + (tw % BS) + (lane >> 5)) * kv_dim;
-    const uint16_t* ks = key_cache + row + k_elem;
-    const uint16_t* vs = value_cache + row + v_elem;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                 :: "s"(lds_addr(buf + 2 * wave * ROWB)), "v"(ks) : "memory", "m0");
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                 :: "s"(lds_addr(buf + V_OFF + 2 * wave * ROWB)), "v"(vs) : "memory", "m0");
+    const size_t row = ((size_t)phys * BS + (tw % BS)) * kv_dim;   // wave-uniform
+    const uint16_t* kb = key_cache + row;
+    const uint16_t* vb = value_cache + row;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :: "s"(lds_addr(buf + 2 * wave * ROWB)), "v"(k_off), "s"(kb) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :: "s"(lds_addr(buf + V_OFF + 2 * wave * ROWB)), "v"(v_off), "s"(vb) : "memory", "m0");
   };
   // s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima.
   constexpr int kWaitVmcnt0 = 0x0F70, kWaitVmcnt2 = 0x0F72;
