@@ -700,3 +700,36 @@ def test_prefill_llama_shape(chunks, cached):
     from workloads import make_prefill_case
     w = make_prefill_case(chunks, cached, 32, 128, "f16", seed=sum(chunks), name="prefill_llama")
     check_prefill(w)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_long_prompt(dtype):
+    """A 16,384-token whole prompt (64 query tiles, 256 key stages) and a
+    1,000-row chunk after a 20,000-token cached prefix, 4 heads x 128. Rows of
+    a causal call depend only on the keys up to them, so the oracle computes
+    windows of rows as chunks of the same sequence (first, middle and last 64
+    rows of each), every head, against the full GPU call."""
+    from workloads import make_prefill_case
+    pkv = _pkv()
+    w = make_prefill_case([16384, 1000], [0, 20000], 4, 128, dtype, seed=41, name="prefill_long")
+    say(f"prefill {w.name}: {dtype} ctx={w.context_lens.tolist()} rows={w.query.shape[0]}")
+    dw = upload(w)
+    pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
+    pkv.paged_attention_prefill(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                dw.context_lens, dw.query_start, w.scale)
+    torch.cuda.synchronize()
+    got = device_to_float64(dw.out)
+    K, V = oracle.reshape_and_cache(w.new_key, w.new_value, w.key_cache, w.value_cache,
+                                    w.slot_mapping, w.block_size)
+    qs = w.query_start
+    for s in range(w.num_seqs):
+        q0, qn = int(qs[s]), int(qs[s + 1] - qs[s])
+        first = int(w.context_lens[s]) - qn
+        for r0 in (0, qn // 2, qn - 64):
+            rows = slice(q0 + r0, q0 + r0 + 64)
+            want = oracle.paged_attention_prefill(
+                w.query[rows], K, V, w.block_tables[s:s + 1],
+                np.array([first + r0 + 64], dtype=np.int32), np.array([0, 64]), w.scale,
+                w.block_size, w.dtype)
+            assert_attention_close(got[rows], want, what=f"seq {s} rows {r0}..{r0 + 63}",
+                                   format_bound="bf16" if dtype == "bf16" else None)
