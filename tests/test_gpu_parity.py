@@ -733,3 +733,18 @@ def test_prefill_long_prompt(dtype):
                 w.block_size, w.dtype)
             assert_attention_close(got[rows], want, what=f"seq {s} rows {r0}..{r0 + 63}",
                                    format_bound="bf16" if dtype == "bf16" else None)
+
+
+@pytest.mark.parametrize("bs,max_blocks", [(16, 37), (8, 75), (32, 19)])
+def test_table_end_inside_partition(bs, max_blocks):
+    """Block tables whose end falls inside a 256-token partition's table
+    entries (37 x 16, 75 x 8, 19 x 32 tokens): a partition loads its entries
+    up to the table's end only, and contexts that fill the table to its last
+    token still read every row. NaN canaries in every unused slot."""
+    full = max_blocks * bs
+    ctx = [full, full - 1, 513, 257, 256, 1]
+    w = make_decode_case(ctx, 4, 128, "f16", seed=bs + max_blocks, max_blocks=max_blocks,
+                         block_size=bs)
+    _, clean = check_full_step(w)
+    _, poisoned = check_full_step(poison_unused(w), check_caches=False)
+    assert np.array_equal(clean, poisoned)
