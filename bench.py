@@ -80,12 +80,14 @@ def parse():
                          "LLaMA-7B shape; prints its own JSON line")
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="element type of the --prefill workloads")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the fp16 prefill records of the default run")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-workload records (workloads 2-5, 5 warm-up + 50 timed "
                          "decode calls each) that the default run adds to its JSON line")
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="turn a rocprofv3 --stats kernel_stats.csv of `bench.py --workload N "
-                         "--no-per-config --no-cpu-baseline` into profiles/kernels_<workload>.md "
+                         "--no-per-config --no-prefill --no-cpu-baseline` into profiles/kernels_<workload>.md "
                          "and exit (no GPU needed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 1 GiB (the known-size reference for "
@@ -242,10 +244,9 @@ def traffic_summary(paths, w, grouped):
     ung = " --ungrouped" if (w.group_start is not None and not grouped) else ""
     if w.block_size != 16:
         ung += f" --block-size {w.block_size}"
-    for ctr, path, prog in (("FETCH_SIZE", paths[0], f"--steps 10 --warmup 2 --no-cpu-baseline "
-                                                     f"--workload {w.index}{ung}"),
-                            ("WRITE_SIZE", paths[1], f"--steps 10 --warmup 2 --no-cpu-baseline "
-                                                     f"--workload {w.index}{ung}"),
+    run_args = f"--no-per-config --no-prefill --no-cpu-baseline --steps 10 --warmup 2 --workload {w.index}{ung}"
+    for ctr, path, prog in (("FETCH_SIZE", paths[0], run_args),
+                            ("WRITE_SIZE", paths[1], run_args),
                             ("FETCH_SIZE", paths[2], "--calibrate-copy"),
                             ("WRITE_SIZE", paths[3], "--calibrate-copy")):
         d = os.path.relpath(os.path.dirname(path), ROOT)
@@ -440,7 +441,9 @@ def prefill_flops(w):
     return int(4 * w.head_dim * w.num_heads * keys.sum())
 
 
-def prefill_bench(args, dev):
+def prefill_records(dtype, steps, block_size, dev):
+    """Time the two prefill workloads (HIP events, median of up to 30 calls
+    after 0.3 s of warm-up); one record per workload."""
     import torch
 
     import paged_kv_cache_159_amd as pkv
@@ -453,11 +456,10 @@ def prefill_bench(args, dev):
                           [0] * 8),
         "chunks_512": ([512] * 16, [int(x) for x in rng.integers(1024, 3072, size=16, endpoint=True)]),
     }
-    res = {"metric": "paged prefill attention TFLOP/s (MFMA)", "unit": "TFLOP/s",
-           "data": "synthetic", "dtype": args.dtype}
+    res = {}
     for name, (chunks, cached) in cases.items():
-        w = make_prefill_case(chunks, cached, 32, 128, args.dtype, seed=len(name),
-                              block_size=args.block_size, name=name)
+        w = make_prefill_case(chunks, cached, 32, 128, dtype, seed=len(name),
+                              block_size=block_size, name=name)
         dw = upload(w, dev)
         pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
         mq = max(chunks)
@@ -477,7 +479,7 @@ def prefill_bench(args, dev):
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
         evs = []
-        for _ in range(max(5, min(args.steps, 30))):
+        for _ in range(max(5, min(steps, 30))):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -491,11 +493,18 @@ def prefill_bench(args, dev):
         tf = fl / (us * 1e-6) / 1e12
         res[name] = {"kernel_us": round(us, 1), "kernel_us_mean": round(float(np.mean(times)), 1),
                      "warmup_calls": n, "flops": fl, "tflops": round(tf, 1),
-                     "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS[args.dtype], 4),
+                     "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS[dtype], 4),
                      "tokens": int(sum(chunks)), "tokens_per_s": round(sum(chunks) / (us * 1e-6), 1),
                      "chunks": chunks, "cached": cached}
         del dw
         torch.cuda.empty_cache()
+    return res
+
+
+def prefill_bench(args, dev):
+    res = {"metric": "paged prefill attention TFLOP/s (MFMA)", "unit": "TFLOP/s",
+           "data": "synthetic", "dtype": args.dtype}
+    res.update(prefill_records(args.dtype, args.steps, args.block_size, dev))
     res["value"] = res["whole_prompts"]["tflops"]
     res["roofline"] = {"bound": "mfma", "achieved": res["whole_prompts"]["tflops"],
                        "peak": MFMA_PEAK_TFLOPS[args.dtype], "unit": "TFLOP/s",
@@ -758,7 +767,7 @@ def per_config_record(index, dev, runs=50, warmup=5, block_size=16):
 
 def stats_summary(csv_path, w, grouped):
     """profiles/kernels_<workload>.md from a rocprofv3 kernel_stats.csv of
-    `bench.py --workload N --no-per-config --no-cpu-baseline`: the kernel
+    `bench.py --workload N --no-per-config --no-prefill --no-cpu-baseline`: the kernel
     table, and the decode kernels' algorithmic bytes over their average
     duration against the 8 TB/s peak."""
     import csv
@@ -785,7 +794,7 @@ def stats_summary(csv_path, w, grouped):
              "rocprofv3 --kernel-trace --stats --output-format csv -d "
              f"{os.path.relpath(os.path.dirname(os.path.abspath(csv_path)), ROOT)} -o "
              f"{os.path.basename(csv_path).split('_kernel_stats')[0]} -- python -u bench.py "
-             f"--workload {w.index}{ung} --no-per-config --no-cpu-baseline", "```", "",
+             f"--workload {w.index}{ung} --no-per-config --no-prefill --no-cpu-baseline", "```", "",
              f"Decode kernel source digest (bench.py `source_digest`): `{source_digest(grouped)}`.", "",
              "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
     for n, c, a, mn, mx, pc in rows:
@@ -982,6 +991,15 @@ def main():
             print(f"[bench] workload {idx}: decode call {rc_['decode_call_us']['p50']} us -> "
                   f"{rc_['decode_call_frac']:.3f} of peak, {rc_['seqs_per_s']:.0f} seqs/s",
                   file=sys.stderr, flush=True)
+    if not args.no_prefill and args.block_size == 16:
+        # f4 beside the decode records: fp16 prefill on MFMA (the --prefill run's workloads)
+        pf = prefill_records("f16", 30, 16, dev)
+        res["prefill_f16"] = {k: {f: v[f] for f in ("kernel_us", "tflops", "frac_of_peak", "tokens",
+                                                    "tokens_per_s")}
+                              for k, v in pf.items()}
+        for k, v in res["prefill_f16"].items():
+            print(f"[bench] prefill {k}: {v['kernel_us']} us -> {v['tflops']} TFLOP/s = "
+                  f"{v['frac_of_peak']:.3f} of the MFMA peak", file=sys.stderr, flush=True)
     res["hbm_measured"] = hbm_context()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
