@@ -326,6 +326,13 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
       // take the causal mask (instantiated apart, so the others skip it).
       auto step = [&](auto mask_tag) {
         constexpr bool kMask = decltype(mask_tag)::value;
+        // Wave priority (fp16): the softmax (a chain of dependent VALU work)
+        // runs at priority 1 and the MFMA blocks at 0, so on a SIMD the wave
+        // in its softmax wins issue slots while the other wave's MFMAs run.
+        // bf16, whose split P doubles the P.V MFMAs, ran 3-4% faster without
+        // the priorities; fp16 1-2% slower. Set before the K reads, so that
+        // the reads and the MFMAs form one scheduling region (below).
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
         uint4 ka[NK], kb[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
@@ -340,22 +347,32 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
                                                     (32 * i + 8 * grp) * 2);
           }
         }
-        // Wave priority (fp16): the softmax (a chain of dependent VALU work)
-        // runs at priority 1 and the MFMA blocks at 0, so on a SIMD the wave
-        // in its softmax wins issue slots while the other wave's MFMAs run.
-        // bf16, whose split P doubles the P.V MFMAs, ran 3-4% faster without
-        // the priorities; fp16 1-2% slower.
-        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+        // S^T by K piece (32 dims) across the query tiles. Each tile's sums
+        // run over the pieces in order, as before; the schedule below issues
+        // the reads of pieces 0 and 1, then each piece's MFMAs with the reads
+        // of the piece two ahead, so only the first reads are waited for
+        // before the matrix cores start (all eight reads first, then a wait
+        // for all of them: fp16 whole prompts 1-2% slower on three boxes).
         f4_t sa[QW], sb[QW];
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
           sa[j] = f4_t{0.f, 0.f, 0.f, 0.f};
           sb[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-          for (int i = 0; i < NK; ++i) {
+        for (int i = 0; i < NK; ++i) {
+#pragma unroll
+          for (int j = 0; j < QW; ++j) {
             sa[j] = M::k32(ka[i], qf[j][i], sa[j]);
             sb[j] = M::k32(kb[i], qf[j][i], sb[j]);
           }
+        }
+        // Scheduling groups (mask 0x100: LDS reads, 0x008: MFMA).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * QW, 0);
+          if (i + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         constexpr bool kSplit = std::is_same<T, BF16>::value;
         uint4 bhi[QW], blo[QW];
