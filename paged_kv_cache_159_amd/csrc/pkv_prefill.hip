@@ -347,12 +347,12 @@ prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
                                                     (32 * i + 8 * grp) * 2);
           }
         }
-        // S^T by K piece (32 dims) across the query tiles. Each tile's sums
-        // run over the pieces in order, as before; the schedule below issues
-        // the reads of pieces 0 and 1, then each piece's MFMAs with the reads
-        // of the piece two ahead, so only the first reads are waited for
-        // before the matrix cores start (all eight reads first, then a wait
-        // for all of them: fp16 whole prompts 1-2% slower on three boxes).
+        // S^T by K piece (32 dims) across the query tiles; each tile's sums
+        // still run over the pieces in order. The schedule below issues the
+        // reads of pieces 0 and 1, then each piece's MFMAs with the reads of
+        // the piece two ahead, so only the first reads are waited for before
+        // the matrix cores start (all eight reads first, then a wait for all
+        // of them: fp16 whole prompts 1-2% slower on three boxes).
         f4_t sa[QW], sb[QW];
 #pragma unroll
         for (int j = 0; j < QW; ++j) {
