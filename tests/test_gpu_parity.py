@@ -241,6 +241,63 @@ def test_one_token_context_returns_v_exactly():
     assert np.array_equal(device_to_bits(dw.out), w.new_value)
 
 
+def _words(x, dtype):
+    """Float values as 16-bit words of the element type (nearest even)."""
+    x = np.asarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _values(words, dtype):
+    if dtype == "f16":
+        return words.view(np.float16).astype(np.float32)
+    return (words.astype(np.uint32) << 16).view(np.float32)
+
+
+def _growing_scores(w, cached=None, norm=None):
+    """Make scores grow along each sequence: dim 0 of every query is 8 and
+    dim 0 of key t of sequence s is 64 t / ctx_s (64 t / norm if given: one
+    value per position, as blocks shared by several sequences need), so the
+    last key's score exceeds the first one's by ~65 in log2 units at the
+    1/sqrt(128) scale (the other dims add about +-1); V is scaled by 1/4.
+    Keys already in the pool are found through the table; the new tokens'
+    keys are in new_key, tokens of sequence s at positions cached[s] ..
+    ctx_s - 1 (decode: ctx_s - 1 only)."""
+    dt, bs = w.dtype, w.block_size
+    w.query[..., 0] = _words(8.0, dt)
+    new_pos = []
+    if cached is None:   # decode: one new token per sequence, at ctx - 1
+        new_pos = [(s, int(c) - 1) for s, c in enumerate(w.context_lens)]
+        old = [int(c) - 1 for c in w.context_lens]
+    else:                # prefill: the chunk after ``cached[s]`` tokens
+        old = list(cached)
+        for s, c in enumerate(w.context_lens):
+            new_pos += [(s, p) for p in range(old[s], int(c))]
+    den = [int(c) if norm is None else norm for c in w.context_lens]
+    for s in range(len(w.context_lens)):
+        t = np.arange(old[s])
+        if len(t):
+            blk = w.block_tables[s, t // bs].astype(np.int64)
+            w.key_cache[blk, t % bs, :, 0] = _words(64.0 * t / den[s], dt)[:, None]
+    for i, (s, p) in enumerate(new_pos):
+        w.new_key[i, :, 0] = _words(64.0 * p / den[s], dt)
+    w.value_cache[...] = _words(_values(w.value_cache, dt) * 0.25, dt)
+    w.new_value[...] = _words(_values(w.new_value, dt) * 0.25, dt)
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_growing_scores(dtype):
+    """Scores rising by ~65 (log2) along the context: each stream's running
+    max moves at every row, and split-K partials of one (sequence, head)
+    differ in max by up to ~60, so the merge weights of the early partitions
+    underflow. 3,000 tokens (12 partitions), 700, 64 and 1."""
+    w = _growing_scores(make_decode_case([3000, 700, 64, 1], 2, 128, dtype, seed=77,
+                                         max_blocks=188))
+    check_full_step(w, format_bound="bf16" if dtype == "bf16" else None)
+
+
 def test_single_sequence_and_many_heads():
     w = make_decode_case([777], 64, 128, "f16", seed=4)
     check_full_step(w)
@@ -322,6 +379,17 @@ def test_grouped_shared_prefix():
     """16 prompts x 8 samples, bf16: 20 shared blocks per group on MFMA, tails
     and the CoW-copied partial block on the partition kernel, one merge."""
     check_grouped(make_config(4))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_grouped_growing_scores(dtype):
+    """The grouped call with scores rising by ~65 (log2) along the context:
+    the MFMA chunks of a 600-token shared prefix and the tails carry partials
+    whose maxima differ by up to ~60 before the merge."""
+    from workloads import make_shared_case
+    w = make_shared_case(2, 4, 600, 1, 100, 2, 128, dtype, seed=93)
+    w = _growing_scores(w, [600] * w.num_seqs, norm=int(w.context_lens.max()))
+    check_grouped(w, format_bound="bf16" if dtype == "bf16" else None)
 
 
 def test_grouped_canaries_not_read():
@@ -700,6 +768,18 @@ def test_prefill_llama_shape(chunks, cached):
     from workloads import make_prefill_case
     w = make_prefill_case(chunks, cached, 32, 128, "f16", seed=sum(chunks), name="prefill_llama")
     check_prefill(w)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_growing_scores(dtype):
+    """Prefill with scores rising by ~65 (log2) along each sequence: the
+    softmax reference of every query row has to move many times (it moves
+    when a score passes it by more than 8), on masked and unmasked steps,
+    in whole prompts and in a chunk after a cached prefix."""
+    from workloads import make_prefill_case
+    cached = [0, 0, 500]
+    w = make_prefill_case([700, 17, 300], cached, 2, 128, dtype, seed=91)
+    check_prefill(_growing_scores(w, cached), format_bound="bf16" if dtype == "bf16" else None)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
