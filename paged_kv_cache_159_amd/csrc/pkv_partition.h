@@ -8,10 +8,16 @@ namespace pkv {
 
 constexpr int kWaves = 8;
 typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
-// 16-token tiles each loop step covers: every wave has 2 * kTilesPerStep rows
-// of K and V in flight per step (two tiles per step measured within +-0.5
-// points of one at the LLaMA-7B, shared-prefix and long-context decodes).
+// 16-token tiles each loop step covers: every wave has 2 * (tiles per step)
+// rows of K and V in flight per step. The plain decode takes one (two
+// measured within +-0.5 points at the LLaMA-7B and long-context decodes);
+// the grouped call's tail partitions take two: they share the machine with
+// the shared-prefix units, and the longest tails bound the launch, so more
+// bytes in flight per tail workgroup shortened the shared-prefix decode
+// (grouped call 70.0-70.3 -> 68.7-69.2 us; block size 8 68.9-69.3 -> 68.2,
+// block size 32 70.0-70.1 -> 68.6-68.9).
 constexpr int kTilesPerStep = 1;
+constexpr int kTailTilesPerStep = 2;
 
 // LDS bytes partition_body needs: per wave and head (max, sum), and per wave a
 // head group's accumulators.
@@ -194,7 +200,8 @@ __device__ __forceinline__ void partition_body(
   using E = Elem<T>;
   constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
   constexpr int HG = 64 / LPR;       // heads per wave-wide load
-  constexpr int STEP = kTileTokens * kTilesPerStep;    // tokens per loop step
+  constexpr int TPS = TAIL ? kTailTilesPerStep : kTilesPerStep;
+  constexpr int STEP = kTileTokens * TPS;             // tokens per loop step
   constexpr int RPW = STEP / kWaves;                  // rows each wave reads per step
   static_assert(PT % BS == 0 && PT % STEP == 0, "partition is whole blocks and steps");
   static_assert(BS % 8 == 0, "rows w, w + 8, ... of a step lie in blocks of >= 8 tokens");
@@ -311,7 +318,7 @@ __device__ __forceinline__ void partition_body(
       // With one tile per step at block sizes >= 16, the tile sits in the
       // block of tb.
       const uint32_t bi =
-          ((kTilesPerStep == 1 && BS >= kTileTokens) ? (uint32_t)tb : te) / BS - tbase;
+          ((TPS == 1 && BS >= kTileTokens) ? (uint32_t)tb : te) / BS - tbase;
       const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(table_lane, bi);
       const uint32_t off = (te % BS) * row_bytes + col_bytes;
       // Non-temporal V loads: a row read once per launch should not displace
