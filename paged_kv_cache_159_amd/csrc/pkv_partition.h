@@ -14,8 +14,8 @@ typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
 // the grouped call's tail partitions take two: they share the machine with
 // the shared-prefix units, and the longest tails bound the launch, so more
 // bytes in flight per tail workgroup shortened the shared-prefix decode
-// (grouped call 70.0-70.3 -> 68.7-69.2 us; block size 8 68.9-69.3 -> 68.2,
-// block size 32 70.0-70.1 -> 68.6-68.9).
+// (grouped call 69.9-70.0 -> 69.2-69.4 us on two boxes; block size 8
+// 69.3-70.0 -> 68.2-68.6, block size 32 70.1-70.4 -> 68.6-69.5).
 constexpr int kTilesPerStep = 1;
 constexpr int kTailTilesPerStep = 2;
 
