@@ -141,11 +141,39 @@ def algorithmic_bytes(w):
     return decode, write, copy, logical
 
 
+def _code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that the digest follows the code and not its commentary. String and
+    character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(grouped=False):
+    """Digest of the code (comments and layout excluded) of the kernels one
+    timed decode launch runs."""
     h = hashlib.sha256()
     for p in (GROUPED_SOURCES if grouped else DECODE_SOURCES):
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
