@@ -106,9 +106,14 @@ const char* pkv_status_string(int status);
  * max_blocks_per_seq*block_size > 4096, or when num_seqs * ceil(num_heads /
  * G) * ceil(max_blocks_per_seq*block_size / 256) >= 8192 (G = 4 heads at
  * head_dim 128, 8 at 64: the heads one workgroup covers), else 256 tokens.
- * Returns 0 when no
- * sequence can span more than one partition or when the arguments are
- * invalid.
+ * For batches of at most 256 sequences and 65,536 (sequence, partition)
+ * slots, the workspace also holds one 32-bit claim flag per (backed-up item,
+ * head group): the last quarter of the launch's work items get a second
+ * workgroup on another XCD, and the flag lets exactly one of the two compute
+ * the item (at the first 256-byte boundary after the partials;
+ * ceil(num_seqs * partitions / 4) * ceil(num_heads / G) flags). Returns 0
+ * when no sequence can span more than one partition or when the arguments
+ * are invalid.
  */
 size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
                                       int max_blocks_per_seq, int block_size);
@@ -126,9 +131,13 @@ size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
  * log-sum-exp; the reduction order depends only
  * on logical token positions, so relabelling physical blocks leaves `out`
  * bit-identical.
- * `workspace` (>= paged_attention_workspace_size(...) bytes, any content) may
- * be NULL when that size is 0. num_seqs == 0 is a no-op (pointers may then be
- * NULL).
+ * `workspace` (>= paged_attention_workspace_size(...) bytes) may be NULL
+ * when that size is 0. Any content gives the correct result; the claim flags
+ * are left as they were found when they started at zero, and zeroing the
+ * workspace once when it is allocated lets the first of an item's two
+ * workgroups compute it (from other values the second one does). Calls that
+ * share a workspace must be ordered (one stream). num_seqs == 0 is a no-op
+ * (pointers may then be NULL).
  * Equivalent to paged_attention_decode_partitions followed by
  * paged_attention_decode_merge on the same stream.
  */
@@ -150,7 +159,8 @@ int paged_attention_decode(void* out, const void* query,
  * partials need more than that (paged_attention_workspace_size(...) >
  * PKV_NOALLOC_SCRATCH_BYTES) returns PKV_ERR_SCRATCH before touching the
  * device. Every call on one GPU shares that GPU's array and leaves its
- * partials in it; nothing in it must start at zero. Calls that overlap on one
+ * partials in it; the array starts at zero and the claim flags in it are
+ * left at zero by every call. Calls that overlap on one
  * GPU (on different streams, or from several threads without ordering) race
  * on the array and may return wrong results: order them on one stream.
  */

@@ -13,6 +13,7 @@
 #include "pkv_device.h"
 #include "pkv_debug.h"
 #include "pkv_launch.h"
+#include "pkv_partition.h"
 
 namespace {
 
@@ -41,6 +42,16 @@ int num_partitions(int num_seqs, int num_heads, int head_dim, int max_blocks_per
   return (int)((tokens + pt - 1) / pt);
 }
 
+// Claim flags of the backed-up items (planned item order only), after the
+// partials at a 256-byte boundary.
+size_t backup_flags_offset(size_t partial_bytes) { return (partial_bytes + 255) & ~(size_t)255; }
+size_t backup_flags_bytes(int num_seqs, int num_heads, int head_dim, int parts) {
+  if (!pkv::plan_fits(num_seqs, parts)) return 0;
+  const int hg = 64 / (head_dim / 8);
+  return (size_t)pkv::backup_capacity(num_seqs, parts) * (size_t)((num_heads + hg - 1) / hg) *
+         sizeof(uint32_t);
+}
+
 // Validation shared by the decode entry points. Fills *parts and *need.
 int check_decode(int num_seqs, int num_heads, int head_dim, int block_size,
                  int max_blocks_per_seq, int* parts, size_t* need) {
@@ -49,6 +60,7 @@ int check_decode(int num_seqs, int num_heads, int head_dim, int block_size,
   *parts = num_partitions(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size);
   if ((int64_t)num_seqs * num_heads * (*parts) > kMaxGrid) return PKV_ERR_SHAPE;
   *need = (*parts > 1) ? pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, *parts) : 0;
+  if (*need) *need = backup_flags_offset(*need) + backup_flags_bytes(num_seqs, num_heads, head_dim, *parts);
   return PKV_OK;
 }
 
@@ -127,7 +139,15 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->ws_ml = nullptr;
   a->ws_o = nullptr;
   a->ws_seq = nullptr;
+  a->flags = nullptr;
+  a->backup_items = 0;
   if (need) pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a->ws_ml, &a->ws_o);
+  if (need && backup_flags_bytes(num_seqs, num_heads, head_dim, parts)) {
+    a->flags = reinterpret_cast<uint32_t*>(
+        static_cast<char*>(workspace) +
+        backup_flags_offset(pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, parts)));
+    a->backup_items = pkv::backup_capacity(num_seqs, parts);
+  }
   return PKV_OK;
 }
 

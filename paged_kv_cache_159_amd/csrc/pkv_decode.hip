@@ -62,7 +62,8 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         int max_blocks, int num_parts, float scale_log2,
                         const int32_t* __restrict__ group_start,
                         const int32_t* __restrict__ shared_blocks, int num_groups,
-                        int slot_base, int32_t* __restrict__ seq_tok0) {
+                        int slot_base, int32_t* __restrict__ seq_tok0,
+                        uint32_t* __restrict__ flags, int backup_items) {
   // The LDS array is sized so that two 8-wave workgroups fit on a CU (the
   // kernel itself needs partition_lds_bytes): with four resident workgroups
   // per CU the LLaMA-7B and long-context decodes measured ~1% slower.
@@ -72,7 +73,7 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
   partition_body<T, D, PT, BS, TAIL>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
                                      block_tables, context_lens, num_seqs, num_heads, max_blocks,
                                      num_parts, scale_log2, group_start, shared_blocks,
-                                     num_groups, slot_base, seq_tok0, lds);
+                                     num_groups, slot_base, seq_tok0, lds, flags, backup_items);
 }
 
 // Log-sum-exp merge of the partials of one (sequence, head). Partials live in
@@ -252,7 +253,10 @@ template <typename T, int D, int PT, int BS, bool TAIL>
 hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
   constexpr int HG = 64 / (D / 8);
   const unsigned groups = (unsigned)(a.num_heads + HG - 1) / HG;
-  const unsigned grid = (unsigned)a.num_seqs * groups * (unsigned)a.tail_parts;
+  unsigned grid = (unsigned)a.num_seqs * groups * (unsigned)a.tail_parts;
+  // backup workgroups of the last items (planned order only)
+  const bool backups = !TAIL && a.flags != nullptr && plan_fits(a.num_seqs, a.num_parts);
+  if (backups) grid += (unsigned)a.backup_items * groups;
   hipLaunchKernelGGL((decode_partition_kernel<T, D, PT, BS, TAIL>), dim3(grid), dim3(kWaves * 64), 0, st,
                      static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o,
                      static_cast<const uint16_t*>(a.query),
@@ -260,7 +264,7 @@ hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
                      static_cast<const uint16_t*>(a.value_cache), a.block_tables, a.context_lens,
                      a.num_seqs, a.num_heads, a.max_blocks_per_seq, a.num_parts,
                      a.scale * kLog2e, a.group_start, a.shared_blocks, a.num_groups, a.slot_base,
-                     a.ws_seq);
+                     a.ws_seq, backups ? a.flags : nullptr, backups ? a.backup_items : 0);
   return hipGetLastError();
 }
 

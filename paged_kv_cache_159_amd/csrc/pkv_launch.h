@@ -40,6 +40,9 @@ struct DecodeArgs {
   float* ws_o;          // [num_seqs][num_heads][num_parts][head_dim] normalised partial outputs
   int32_t* ws_seq;      // grouped call: [num_seqs] shared-prefix tokens of each sequence,
                         // written by the main launch, read by the merge
+  uint32_t* flags;      // plain call with a planned item order: claim flags of the
+                        // backed-up items, [backup_items][head groups]
+  int backup_items;
 };
 
 // Tokens per context partition for these sizes (256 or 512): 512 for tables

@@ -48,14 +48,35 @@ constexpr int partition_lds_bytes() {
 constexpr int kPlanMaxSeqs = 256;   // context lengths held in registers (4 per lane)
 constexpr int kRemClasses = 8;
 
-// Item of grid slot sp (of num_seqs * num_parts slots): sequence s, partition
-// p and the sequence's context length ctx (read from the registers the plan
-// already holds); false for a slot with no item. Computed by each wave from
-// the context lengths (one load per lane and 64 sequences), wave-uniform.
+// Backed-up items. The XCDs of one MI355X run the same work at different
+// speeds (per-workgroup timestamps: up to ~10% apart, which XCDs are slow
+// varies by box), and the hardware hands every XCD the same share of the
+// grid. So the last quarter of the item order (at most backup_capacity items)
+// also gets a second, backup workgroup, appended to the grid on the next XCD:
+// whichever of the two claims the item first computes it, the other exits.
+// An XCD that has run through its own share takes over a slower XCD's last
+// items. Measured on MI355X (decode call, HIP-event medians, interleaved
+// runs): 8 x 32K tokens 635-638 -> 627 us on three runs (the XCDs' end
+// times 570-629 -> 602-621 us), 256 of Exp(512) -0.3 to -0.6%, 64 of
+// U[128, 2048] -0.1 to -0.5%. Backing up half the order instead cost the
+// shorter batches 2-3% (every backed-up item pays a claim before its loads).
+__host__ __device__ inline int backup_capacity(int num_seqs, int num_parts) {
+  return (num_seqs * num_parts + 3) / 4;
+}
+
+// Item of grid slot sp (of num_seqs * num_parts slots), or with bk >= 0 the
+// item of backup workgroup bk (the bk-th item of the backed-up range, the
+// last B of the N items, B = min(backup_items, ceil(N / 4))): sequence s,
+// partition p and the sequence's context length ctx (read from the registers
+// the plan already holds); false for a slot or backup with no item. claim_k
+// is the item's index in the backed-up range, -1 outside it. Computed by each
+// wave from the context lengths (one load per lane and 64 sequences),
+// wave-uniform.
 template <int PT>
-__device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
+__device__ __forceinline__ bool plan_item(int sp, int bk, int backup_items, int num_seqs,
+                                          int num_parts,
                                           const int32_t* __restrict__ context_lens, int& s,
-                                          int& p, int& ctx) {
+                                          int& p, int& ctx, int& claim_k) {
   constexpr int KC = kPlanMaxSeqs / 64;
   const int lane = threadIdx.x & 63;
   int cl[KC];
@@ -86,8 +107,16 @@ __device__ __forceinline__ bool plan_item(int sp, int num_seqs, int num_parts,
   // sequences (~11,000 empty workgroups, each loading the context lengths,
   // run after the real work has drained).
   const uint32_t NP = (uint32_t)num_seqs * (uint32_t)num_parts;
-  const uint32_t i = ((uint32_t)sp * N + NP - 1) / NP;
-  if (i >= N || (i * NP) / N != (uint32_t)sp) return false;
+  const uint32_t B = min((uint32_t)backup_items, (N + 3) / 4);   // backed-up items: [N - B, N)
+  uint32_t i;
+  if (bk < 0) {
+    i = ((uint32_t)sp * N + NP - 1) / NP;
+    if (i >= N || (i * NP) / N != (uint32_t)sp) return false;
+  } else {
+    if ((uint32_t)bk >= B) return false;
+    i = N - B + (uint32_t)bk;
+  }
+  claim_k = i >= N - B ? (int)(i - (N - B)) : -1;
   if ((int)i < F) {
     int j = (int)i;
 #pragma unroll
@@ -196,7 +225,8 @@ __device__ __forceinline__ void partition_body(
     const int32_t* __restrict__ context_lens, int num_seqs, int num_heads, int max_blocks,
     int num_parts, float scale_log2, const int32_t* __restrict__ group_start,
     const int32_t* __restrict__ shared_blocks, int num_groups, int slot_base,
-    int32_t* __restrict__ seq_tok0, uint8_t* lds) {
+    int32_t* __restrict__ seq_tok0, uint8_t* lds, uint32_t* __restrict__ flags = nullptr,
+    int backup_items = 0) {
   using E = Elem<T>;
   constexpr int LPR = D / 8;         // lanes per head row (16 bytes each)
   constexpr int HG = 64 / LPR;       // heads per wave-wide load
@@ -209,8 +239,17 @@ __device__ __forceinline__ void partition_body(
 
   const int H = num_heads;
   const int groups = (H + HG - 1) / HG;
-  const int g = wg % groups;
-  const int sp = wg / groups;
+  // Workgroups past the grid's num_seqs * num_parts slots are backups (only
+  // when flags are given): backup bk takes the head group one below its
+  // position's, so it runs on the XCD after the one its item's first
+  // workgroup runs on (the hardware deals workgroup ids to the 8 XCDs in
+  // turn, and the slots hold whole multiples of 8 workgroups at head size 128).
+  const int prim_wgs = num_seqs * num_parts * groups;
+  const bool is_backup = !TAIL && wg >= prim_wgs;
+  const int g = is_backup ? ((wg - prim_wgs) % groups + groups - 1) % groups : wg % groups;
+  const int sp = is_backup ? 0 : wg / groups;
+  const int bk = is_backup ? (wg - prim_wgs) / groups : -1;
+  int claim_k = -1;
   int s = sp % num_seqs;
   int p = sp / num_seqs;
   if constexpr (TAIL) {
@@ -223,7 +262,8 @@ __device__ __forceinline__ void partition_body(
   if constexpr (!TAIL) {
     if (plan_fits(num_seqs, num_parts)) {
       int ps = 0, pp = 0, pc = 0;
-      const bool real = plan_item<PT>(sp, num_seqs, num_parts, context_lens, ps, pp, pc);
+      const bool real = plan_item<PT>(sp, flags ? bk : -1, flags ? backup_items : 0, num_seqs,
+                                      num_parts, context_lens, ps, pp, pc, claim_k);
       // an item outside the grid's (sequence, partition) range is never
       // produced; the bound keeps every later index inside the arrays anyway
       if (!real || (unsigned)ps >= (unsigned)num_seqs || (unsigned)pp >= (unsigned)num_parts)
@@ -263,6 +303,23 @@ __device__ __forceinline__ void partition_body(
     // the ones its tokens use, loaded without waiting for the context length.
     const int e = p * (PT / BS) + lane;
     table_spec = (lane < PT / BS && e < max_blocks) ? block_tables[(size_t)s * max_blocks + e] : 0;
+  }
+  if (claim_k >= 0) {
+    // A backed-up item: its flag is claimed exactly twice per launch (first
+    // and backup workgroup) with a wrapping increment that counts 0 -> 1 -> 0,
+    // and the claim that finds 0 computes the item. From a zeroed flag the
+    // first arrival wins and the flag ends at zero again; from any other
+    // value the second claim finds 0, so exactly one workgroup computes the
+    // item whatever the workspace held. Issued after the query and table
+    // loads, which fly meanwhile.
+    __shared__ uint32_t s_won;
+    if (threadIdx.x == 0) {
+      const uint32_t old = __builtin_amdgcn_atomic_inc32(
+          flags + (size_t)claim_k * groups + g, 1u, __ATOMIC_RELAXED, "agent");
+      s_won = old == 0u;
+    }
+    __syncthreads();
+    if (!s_won) return;
   }
   const int ctx = planned_ctx >= 0 ? planned_ctx : context_lens[s];
   int tok0 = 0;   // first token this launch covers for sequence s

@@ -69,8 +69,11 @@ def workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_blocks_per_
 
 def alloc_workspace(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size=16,
                     device="cuda"):
+    """A zeroed decode workspace: any content gives the same result, and zeroed
+    claim flags let the first of a backed-up item's two workgroups compute it
+    (the calls leave the flags at zero)."""
     n = workspace_size(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def _block_size(key_cache, block_size):

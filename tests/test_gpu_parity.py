@@ -828,3 +828,63 @@ def test_table_end_inside_partition(bs, max_blocks):
     _, clean = check_full_step(w)
     _, poisoned = check_full_step(poison_unused(w), check_caches=False)
     assert np.array_equal(clean, poisoned)
+
+
+def _flags_region(S, H, D, P):
+    """Byte range of the decode workspace's claim flags (after the partials at
+    a 256-byte boundary; ceil(S * P / 4) backed-up items x head groups)."""
+    n = S * H * P
+    partials = ((n * 8 + 255) // 256) * 256 + n * D * 4
+    start = ((partials + 255) // 256) * 256
+    groups = -(-H // (4 if D == 128 else 8))
+    return start, start + -(-(S * P) // 4) * groups * 4
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backup_claims_any_workspace_content(dtype):
+    """The last quarter of the item order runs as two workgroups on different
+    XCDs and a per-item flag lets one compute it. From a workspace of 0xFF
+    bytes (flags at 0xFFFFFFFF, partials NaN) the output is bit-identical to
+    the zeroed-workspace run and meets the oracle bar; from zeroed flags every
+    flag is zero again after the call; a second call from the flags the
+    poisoned run left is still bit-identical."""
+    pkv = _pkv()
+    ctx = [3000, 2900, 2500, 2047, 1500, 1200, 999, 640, 513, 300, 257, 100, 17, 3000, 2222, 1]
+    w = make_decode_case(ctx, 8, 128, dtype, seed=61)
+    dw = upload(w)
+    pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
+    S, H, D, MB = w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq
+    P = -(-(MB * 16) // 256)
+    n = pkv.workspace_size(S, H, D, MB)
+    lo, hi = _flags_region(S, H, D, P)
+    assert hi == n and hi > lo, (lo, hi, n)
+    ws0 = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out0 = torch.empty_like(dw.query)
+    pkv.paged_attention_decode(out0, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                               dw.context_lens, w.scale, workspace=ws0)
+    torch.cuda.synchronize()
+    assert int(ws0[lo:hi].count_nonzero()) == 0, "flags not left at zero"
+    ws1 = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+    out1 = torch.empty_like(dw.query)
+    pkv.paged_attention_decode(out1, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                               dw.context_lens, w.scale, workspace=ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    # the flags of the B backed-up items (B = ceil(N / 4) of the N real items)
+    # end at 0 or 1; the rest of the region is never touched
+    N = sum(-(-c // 256) for c in ctx)
+    used = min(-(-(S * P) // 4), -(-N // 4)) * (H // 4)
+    flags = ws1[lo:hi].view(torch.int32)
+    assert int(((flags[:used] != 0) & (flags[:used] != 1)).sum()) == 0, "a claimed flag outside {0, 1}"
+    assert int((flags[used:] != -1).sum()) == 0, "a flag past the backed-up items was written"
+    out2 = torch.empty_like(dw.query)
+    pkv.paged_attention_decode(out2, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                               dw.context_lens, w.scale, workspace=ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out2.view(torch.int16))
+    K, V = oracle.reshape_and_cache(w.new_key, w.new_value, w.key_cache, w.value_cache,
+                                    w.slot_mapping, w.block_size)
+    want = oracle.paged_attention_decode(w.query, K, V, w.block_tables, w.context_lens, w.scale,
+                                         w.block_size, w.dtype)
+    assert_attention_close(device_to_float64(out1), want, what=f"backup claims {dtype}",
+                           format_bound=dtype if dtype == "bf16" else None)
