@@ -42,11 +42,21 @@ int num_partitions(int num_seqs, int num_heads, int head_dim, int max_blocks_per
   return (int)((tokens + pt - 1) / pt);
 }
 
-// Claim flags of the backed-up items (planned item order only), after the
-// partials at a 256-byte boundary.
+// Claim flags of the backed-up items, after the partials at a 256-byte
+// boundary. Only planned item orders over 512-token partitions back items up:
+// their items are long enough that a slow XCD's lag is worth a claim
+// (measured on MI355X, backups in every planned order: 8 x 32K tokens 634.4
+// -> 626.6 us and 256 of Exp(512) 340.3 -> 338.8 us, both 512-token
+// partitions; 64 of U[128, 2048] (256-token partitions) 166.8 -> 166.6 us;
+// beam search through the plain call, 128 beams over shared prompt blocks
+// (256-token partitions), 113.6 -> 117.8 us per step).
 size_t backup_flags_offset(size_t partial_bytes) { return (partial_bytes + 255) & ~(size_t)255; }
-size_t backup_flags_bytes(int num_seqs, int num_heads, int head_dim, int parts) {
+size_t backup_flags_bytes(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
+                          int block_size, int parts) {
   if (!pkv::plan_fits(num_seqs, parts)) return 0;
+  if (pkv::decode_partition_tokens(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                   block_size) != 512)
+    return 0;
   const int hg = 64 / (head_dim / 8);
   return (size_t)pkv::backup_capacity(num_seqs, parts) * (size_t)((num_heads + hg - 1) / hg) *
          sizeof(uint32_t);
@@ -60,7 +70,9 @@ int check_decode(int num_seqs, int num_heads, int head_dim, int block_size,
   *parts = num_partitions(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size);
   if ((int64_t)num_seqs * num_heads * (*parts) > kMaxGrid) return PKV_ERR_SHAPE;
   *need = (*parts > 1) ? pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, *parts) : 0;
-  if (*need) *need = backup_flags_offset(*need) + backup_flags_bytes(num_seqs, num_heads, head_dim, *parts);
+  if (*need)
+    *need = backup_flags_offset(*need) + backup_flags_bytes(num_seqs, num_heads, head_dim,
+                                                            max_blocks_per_seq, block_size, *parts);
   return PKV_OK;
 }
 
@@ -142,7 +154,8 @@ int prepare_decode(pkv::DecodeArgs* a, void* out, const void* query, const void*
   a->flags = nullptr;
   a->backup_items = 0;
   if (need) pkv::decode_workspace_split(workspace, num_seqs, num_heads, parts, &a->ws_ml, &a->ws_o);
-  if (need && backup_flags_bytes(num_seqs, num_heads, head_dim, parts)) {
+  if (need && backup_flags_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
+                                 parts)) {
     a->flags = reinterpret_cast<uint32_t*>(
         static_cast<char*>(workspace) +
         backup_flags_offset(pkv::decode_workspace_bytes(num_seqs, num_heads, head_dim, parts)));

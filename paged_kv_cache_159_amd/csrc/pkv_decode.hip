@@ -51,7 +51,7 @@ namespace pkv {
 // of LDS per CU holds two of them, not three).
 constexpr int kPartitionOccupancyLds = 60 * 1024;
 
-template <typename T, int D, int PT, int BS, bool TAIL>
+template <typename T, int D, int PT, int BS, bool TAIL, bool BACKUP>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
                         float* __restrict__ ws_o, const uint16_t* __restrict__ query,
@@ -70,7 +70,7 @@ decode_partition_kernel(uint16_t* __restrict__ out, float* __restrict__ ws_ml,
   constexpr int kLds = partition_lds_bytes<D>() > kPartitionOccupancyLds ? partition_lds_bytes<D>()
                                                                         : kPartitionOccupancyLds;
   __shared__ __align__(16) uint8_t lds[kLds];
-  partition_body<T, D, PT, BS, TAIL>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
+  partition_body<T, D, PT, BS, TAIL, BACKUP>(blockIdx.x, out, ws_ml, ws_o, query, key_cache, value_cache,
                                      block_tables, context_lens, num_seqs, num_heads, max_blocks,
                                      num_parts, scale_log2, group_start, shared_blocks,
                                      num_groups, slot_base, seq_tok0, lds, flags, backup_items);
@@ -249,33 +249,35 @@ void decode_workspace_split(void* ws, int num_seqs, int num_heads, int num_parts
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int D, int PT, int BS, bool TAIL>
+template <typename T, int D, int PT, int BS, bool TAIL, bool BACKUP>
 hipError_t partitions_t(const DecodeArgs& a, hipStream_t st) {
   constexpr int HG = 64 / (D / 8);
   const unsigned groups = (unsigned)(a.num_heads + HG - 1) / HG;
   unsigned grid = (unsigned)a.num_seqs * groups * (unsigned)a.tail_parts;
-  // backup workgroups of the last items (planned order only)
-  const bool backups = !TAIL && a.flags != nullptr && plan_fits(a.num_seqs, a.num_parts);
-  if (backups) grid += (unsigned)a.backup_items * groups;
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, PT, BS, TAIL>), dim3(grid), dim3(kWaves * 64), 0, st,
+  if (BACKUP) grid += (unsigned)a.backup_items * groups;   // backup workgroups of the last items
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, PT, BS, TAIL, BACKUP>), dim3(grid), dim3(kWaves * 64), 0, st,
                      static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_o,
                      static_cast<const uint16_t*>(a.query),
                      static_cast<const uint16_t*>(a.key_cache),
                      static_cast<const uint16_t*>(a.value_cache), a.block_tables, a.context_lens,
                      a.num_seqs, a.num_heads, a.max_blocks_per_seq, a.num_parts,
                      a.scale * kLog2e, a.group_start, a.shared_blocks, a.num_groups, a.slot_base,
-                     a.ws_seq, backups ? a.flags : nullptr, backups ? a.backup_items : 0);
+                     a.ws_seq, BACKUP ? a.flags : nullptr, BACKUP ? a.backup_items : 0);
   return hipGetLastError();
 }
 
 template <typename T, int D, int BS>
 hipError_t partitions_b(const DecodeArgs& a, hipStream_t st) {
   const bool tail = a.group_start != nullptr;
+  // backups only where the host gave claim flags: planned orders over
+  // 512-token partitions
+  const bool backup = !tail && a.flags != nullptr && plan_fits(a.num_seqs, a.num_parts);
   if (a.part_tokens == 256)
-    return tail ? partitions_t<T, D, 256, BS, true>(a, st)
-                : partitions_t<T, D, 256, BS, false>(a, st);
-  return tail ? partitions_t<T, D, 512, BS, true>(a, st)
-              : partitions_t<T, D, 512, BS, false>(a, st);
+    return tail ? partitions_t<T, D, 256, BS, true, false>(a, st)
+                : partitions_t<T, D, 256, BS, false, false>(a, st);
+  if (tail) return partitions_t<T, D, 512, BS, true, false>(a, st);
+  return backup ? partitions_t<T, D, 512, BS, false, true>(a, st)
+                : partitions_t<T, D, 512, BS, false, false>(a, st);
 }
 
 template <typename T, int D>

@@ -72,7 +72,7 @@ __host__ __device__ inline int backup_capacity(int num_seqs, int num_parts) {
 // is the item's index in the backed-up range, -1 outside it. Computed by each
 // wave from the context lengths (one load per lane and 64 sequences),
 // wave-uniform.
-template <int PT>
+template <int PT, bool BACKUP>
 __device__ __forceinline__ bool plan_item(int sp, int bk, int backup_items, int num_seqs,
                                           int num_parts,
                                           const int32_t* __restrict__ context_lens, int& s,
@@ -107,16 +107,21 @@ __device__ __forceinline__ bool plan_item(int sp, int bk, int backup_items, int 
   // sequences (~11,000 empty workgroups, each loading the context lengths,
   // run after the real work has drained).
   const uint32_t NP = (uint32_t)num_seqs * (uint32_t)num_parts;
-  const uint32_t B = min((uint32_t)backup_items, (N + 3) / 4);   // backed-up items: [N - B, N)
   uint32_t i;
-  if (bk < 0) {
+  if constexpr (BACKUP) {
+    const uint32_t B = min((uint32_t)backup_items, (N + 3) / 4);   // backed-up items: [N - B, N)
+    if (bk < 0) {
+      i = ((uint32_t)sp * N + NP - 1) / NP;
+      if (i >= N || (i * NP) / N != (uint32_t)sp) return false;
+    } else {
+      if ((uint32_t)bk >= B) return false;
+      i = N - B + (uint32_t)bk;
+    }
+    claim_k = i >= N - B ? (int)(i - (N - B)) : -1;
+  } else {
     i = ((uint32_t)sp * N + NP - 1) / NP;
     if (i >= N || (i * NP) / N != (uint32_t)sp) return false;
-  } else {
-    if ((uint32_t)bk >= B) return false;
-    i = N - B + (uint32_t)bk;
   }
-  claim_k = i >= N - B ? (int)(i - (N - B)) : -1;
   if ((int)i < F) {
     int j = (int)i;
 #pragma unroll
@@ -217,7 +222,7 @@ __host__ __device__ constexpr bool plan_fits(int num_seqs, int num_parts) {
 // shared-prefix units), its partitions go to partial slots slot_base + p,
 // every partition writes a partial (the merge always runs), and the sequence's
 // shared-prefix token count goes to seq_tok0[s] for the merge.
-template <typename T, int D, int PT, int BS, bool TAIL>
+template <typename T, int D, int PT, int BS, bool TAIL, bool BACKUP = false>
 __device__ __forceinline__ void partition_body(
     int wg, uint16_t* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_cache,
@@ -239,13 +244,14 @@ __device__ __forceinline__ void partition_body(
 
   const int H = num_heads;
   const int groups = (H + HG - 1) / HG;
-  // Workgroups past the grid's num_seqs * num_parts slots are backups (only
-  // when flags are given): backup bk takes the head group one below its
-  // position's, so it runs on the XCD after the one its item's first
-  // workgroup runs on (the hardware deals workgroup ids to the 8 XCDs in
-  // turn, and the slots hold whole multiples of 8 workgroups at head size 128).
+  // BACKUP: workgroups past the grid's num_seqs * num_parts slots are
+  // backups: backup bk takes the head group one below its position's, so it
+  // runs on the XCD after the one its item's first workgroup runs on (the
+  // hardware deals workgroup ids to the 8 XCDs in turn, and the slots hold
+  // whole multiples of 8 workgroups at head size 128).
+  static_assert(!(TAIL && BACKUP), "backups are for the planned plain order");
   const int prim_wgs = num_seqs * num_parts * groups;
-  const bool is_backup = !TAIL && wg >= prim_wgs;
+  const bool is_backup = BACKUP && wg >= prim_wgs;
   const int g = is_backup ? ((wg - prim_wgs) % groups + groups - 1) % groups : wg % groups;
   const int sp = is_backup ? 0 : wg / groups;
   const int bk = is_backup ? (wg - prim_wgs) / groups : -1;
@@ -262,8 +268,8 @@ __device__ __forceinline__ void partition_body(
   if constexpr (!TAIL) {
     if (plan_fits(num_seqs, num_parts)) {
       int ps = 0, pp = 0, pc = 0;
-      const bool real = plan_item<PT>(sp, flags ? bk : -1, flags ? backup_items : 0, num_seqs,
-                                      num_parts, context_lens, ps, pp, pc, claim_k);
+      const bool real = plan_item<PT, BACKUP>(sp, bk, backup_items, num_seqs, num_parts,
+                                              context_lens, ps, pp, pc, claim_k);
       // an item outside the grid's (sequence, partition) range is never
       // produced; the bound keeps every later index inside the arrays anyway
       if (!real || (unsigned)ps >= (unsigned)num_seqs || (unsigned)pp >= (unsigned)num_parts)
@@ -304,7 +310,7 @@ __device__ __forceinline__ void partition_body(
     const int e = p * (PT / BS) + lane;
     table_spec = (lane < PT / BS && e < max_blocks) ? block_tables[(size_t)s * max_blocks + e] : 0;
   }
-  if (claim_k >= 0) {
+  if (BACKUP && claim_k >= 0) {
     // A backed-up item: its flag is claimed exactly twice per launch (first
     // and backup workgroup) with a wrapping increment that counts 0 -> 1 -> 0,
     // and the claim that finds 0 computes the item. From a zeroed flag the

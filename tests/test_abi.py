@@ -61,7 +61,7 @@ def _expected_workspace(S, H, D, MB, bs=16):
         return 0
     n = S * H * P
     partials = ((n * 8 + 255) // 256) * 256 + n * D * 4
-    if S <= 256 and S * P <= 65536:     # planned item order: claim flags of the backed-up items
+    if S <= 256 and S * P <= 65536 and pt == 512:   # claim flags of the backed-up items
         return ((partials + 255) // 256) * 256 + -(-(S * P) // 4) * groups * 4
     return partials
 
@@ -71,14 +71,14 @@ def test_workspace_size(L):
     for S, H, D, MB in ((4, 4, 64, 17), (64, 32, 128, 32), (64, 32, 128, 128), (64, 32, 128, 256),
                         (64, 32, 128, 257), (8, 32, 128, 2048), (3, 5, 64, 1000)):
         assert L.paged_attention_workspace_size(S, H, D, MB, 16) == _expected_workspace(S, H, D, MB)
-    # partials (m, l and 128 floats per partition), then 64 * 8 / 4 = 128 backed-up items x 8
-    # head groups of 4-byte flags
-    assert _expected_workspace(64, 32, 128, 128) == 64 * 32 * 8 * 8 + 64 * 32 * 8 * 512 + 128 * 8 * 4
-    # 128 sequences x 8 head groups x 8 slots = 8192: 512-token partitions
+    # 256-token partitions: partials only (m, l and 128 floats per partition)
+    assert _expected_workspace(64, 32, 128, 128) == 64 * 32 * 8 * 8 + 64 * 32 * 8 * 512
+    # 128 sequences x 8 head groups x 8 slots = 8192: 512-token partitions, then the claim
+    # flags of 128 * 4 / 4 = 128 backed-up items x 8 head groups
     assert _expected_workspace(128, 32, 128, 128) == 128 * 32 * 4 * 8 + 128 * 32 * 4 * 512 + 128 * 8 * 4
     # partials, then ceil(S * partitions / 4) flags per head group
     assert L.paged_attention_workspace_size(128, 32, 128, 128, 16) == 128 * 32 * 4 * 520 + 128 * 8 * 4
-    assert L.paged_attention_workspace_size(127, 32, 128, 128, 16) == 127 * 32 * 8 * 520 + 254 * 8 * 4
+    assert L.paged_attention_workspace_size(127, 32, 128, 128, 16) == 127 * 32 * 8 * 520
     # more than 256 sequences: no planned order, no flags
     assert L.paged_attention_workspace_size(300, 32, 128, 128, 16) == _expected_workspace(300, 32, 128, 128)
     assert _expected_workspace(300, 32, 128, 128) == 300 * 32 * 4 * 520

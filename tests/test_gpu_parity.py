@@ -849,12 +849,13 @@ def test_backup_claims_any_workspace_content(dtype):
     flag is zero again after the call; a second call from the flags the
     poisoned run left is still bit-identical."""
     pkv = _pkv()
-    ctx = [3000, 2900, 2500, 2047, 1500, 1200, 999, 640, 513, 300, 257, 100, 17, 3000, 2222, 1]
+    # tables past 4096 tokens: 512-token partitions, whose planned order has backups
+    ctx = [6000, 5900, 4500, 4097, 3000, 2200, 999, 640, 513, 300, 257, 100, 17, 6000, 5222, 1]
     w = make_decode_case(ctx, 8, 128, dtype, seed=61)
     dw = upload(w)
     pkv.reshape_and_cache(dw.new_key, dw.new_value, dw.key_cache, dw.value_cache, dw.slot_mapping)
     S, H, D, MB = w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq
-    P = -(-(MB * 16) // 256)
+    P = -(-(MB * 16) // 512)
     n = pkv.workspace_size(S, H, D, MB)
     lo, hi = _flags_region(S, H, D, P)
     assert hi == n and hi > lo, (lo, hi, n)
@@ -872,7 +873,7 @@ def test_backup_claims_any_workspace_content(dtype):
     assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
     # the flags of the B backed-up items (B = ceil(N / 4) of the N real items)
     # end at 0 or 1; the rest of the region is never touched
-    N = sum(-(-c // 256) for c in ctx)
+    N = sum(-(-c // 512) for c in ctx)
     used = min(-(-(S * P) // 4), -(-N // 4)) * (H // 4)
     flags = ws1[lo:hi].view(torch.int32)
     assert int(((flags[:used] != 0) & (flags[:used] != 1)).sum()) == 0, "a claimed flag outside {0, 1}"
