@@ -106,12 +106,12 @@ const char* pkv_status_string(int status);
  * max_blocks_per_seq*block_size > 4096, or when num_seqs * ceil(num_heads /
  * G) * ceil(max_blocks_per_seq*block_size / 256) >= 8192 (G = 4 heads at
  * head_dim 128, 8 at 64: the heads one workgroup covers), else 256 tokens.
- * For batches of at most 256 sequences and 65,536 (sequence, partition)
- * slots, the workspace also holds one 32-bit claim flag per (backed-up item,
- * head group): the last quarter of the launch's work items get a second
- * workgroup on another XCD, and the flag lets exactly one of the two compute
- * the item (at the first 256-byte boundary after the partials;
- * ceil(num_seqs * partitions / 4) * ceil(num_heads / G) flags). Returns 0
+ * With 512-token partitions, at most 256 sequences and at most 65,536
+ * (sequence, partition) slots, the workspace also holds one 32-bit claim flag
+ * per (backed-up item, head group): the last quarter of the launch's work
+ * items get a second workgroup on another XCD, and the flag lets exactly one
+ * of the two compute the item (at the first 256-byte boundary after the
+ * partials; ceil(num_seqs * partitions / 4) * ceil(num_heads / G) flags). Returns 0
  * when no sequence can span more than one partition or when the arguments
  * are invalid.
  */
