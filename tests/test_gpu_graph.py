@@ -62,6 +62,39 @@ def test_graph_decode_replays():
         assert torch.equal(out_g, out_e), f"replay {r}"
 
 
+def test_graph_decode_backups_replays():
+    """The long-table decode (512-token partitions), whose last items run as
+    two workgroups that claim a flag in the workspace: replays and the eager
+    calls between them share the flags, every replay is bit-identical to the
+    eager call, and the flags end at zero."""
+    say("paged_attention_decode with backup workgroups in a graph, 4 replays")
+    pkv = _pkv()
+    w = make_decode_case([6000, 300, 5000, 1, 4097, 2500, 6400, 777], 8, 128, "bf16", seed=35,
+                         max_blocks=400)
+    dw = upload(w)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq)
+    out_g = torch.empty_like(dw.query)
+    out_e = torch.empty_like(dw.query)
+    g = capture(lambda: pkv.paged_attention_decode(out_g, dw.query, dw.key_cache, dw.value_cache,
+                                                   dw.block_tables, dw.context_lens, w.scale,
+                                                   workspace=ws))
+    gen = torch.Generator(device="cuda").manual_seed(8)
+    for r in range(REPLAYS):
+        dw.query.copy_(torch.randn(dw.query.shape, generator=gen, device="cuda").to(dw.query.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        pkv.paged_attention_decode(out_e, dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                                   dw.context_lens, w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {r}"
+    # partials (8 x 8 heads x 13 partitions), then the flags at the next 256-byte boundary
+    n = 8 * 8 * 13
+    flags_at = (((n * 8 + 255) // 256) * 256 + n * 128 * 4 + 255) // 256 * 256
+    assert ws.numel() == flags_at + -(-(8 * 13) // 4) * 2 * 4
+    assert int(ws[flags_at:].count_nonzero()) == 0, "claim flags not back at zero"
+
+
 def test_graph_grouped_decode_replays():
     say("paged_attention_decode_grouped in a graph, 4 replays")
     pkv = _pkv()
