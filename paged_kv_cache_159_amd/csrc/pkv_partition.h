@@ -55,11 +55,14 @@ constexpr int kRemClasses = 8;
 // also gets a second, backup workgroup, appended to the grid on the next XCD:
 // whichever of the two claims the item first computes it, the other exits.
 // An XCD that has run through its own share takes over a slower XCD's last
-// items. Measured on MI355X (decode call, HIP-event medians, interleaved
-// runs): 8 x 32K tokens 635-638 -> 627 us on three runs (the XCDs' end
-// times 570-629 -> 602-621 us), 256 of Exp(512) -0.3 to -0.6%, 64 of
-// U[128, 2048] -0.1 to -0.5%. Backing up half the order instead cost the
-// shorter batches 2-3% (every backed-up item pays a claim before its loads).
+// items. The host gives claim flags (and so backups) only to planned orders
+// over 512-token partitions, whose items are long. Measured on MI355X
+// (decode call, HIP-event medians, interleaved runs): 8 x 32K tokens
+// 634-638 -> 625-627 us on five runs (the XCDs' end times 570-629 -> 602-621
+// us), 256 of Exp(512) 340-342 -> 338-340 us. Over 256-token partitions the
+// backups gained nothing at 64 of U[128, 2048] and cost beam search through
+// the plain call 4% (short items over shared blocks pay the claim for
+// little); backing up half the order instead of a quarter cost 2-3%.
 __host__ __device__ inline int backup_capacity(int num_seqs, int num_parts) {
   return (num_seqs * num_parts + 3) / 4;
 }
