@@ -159,8 +159,8 @@ int paged_attention_decode(void* out, const void* query,
  * partials need more than that (paged_attention_workspace_size(...) >
  * PKV_NOALLOC_SCRATCH_BYTES) returns PKV_ERR_SCRATCH before touching the
  * device. Every call on one GPU shares that GPU's array and leaves its
- * partials in it; the array starts at zero and the claim flags in it are
- * left at zero by every call. Calls that overlap on one
+ * partials in it; nothing in it must start at zero (the claim flags give the
+ * correct result from any content). Calls that overlap on one
  * GPU (on different streams, or from several threads without ordering) race
  * on the array and may return wrong results: order them on one stream.
  */
