@@ -132,10 +132,10 @@ size_t paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
  * on logical token positions, so relabelling physical blocks leaves `out`
  * bit-identical.
  * `workspace` (>= paged_attention_workspace_size(...) bytes) may be NULL
- * when that size is 0. Any content gives the correct result; the claim flags
- * are left as they were found when they started at zero, and zeroing the
- * workspace once when it is allocated lets the first of an item's two
- * workgroups compute it (from other values the second one does). Calls that
+ * when that size is 0. Any content gives the correct result. Claim flags that
+ * start at zero are left at zero, so zeroing the workspace once when it is
+ * allocated lets the first of an item's two workgroups compute it in every
+ * call (from other values the second one does). Calls that
  * share a workspace must be ordered (one stream). num_seqs == 0 is a no-op
  * (pointers may then be NULL).
  * Equivalent to paged_attention_decode_partitions followed by
