@@ -184,6 +184,23 @@ decode_merge_packed_kernel(uint16_t* __restrict__ out, const float* __restrict__
   const int s = blockIdx.x / hblocks;
   const int h = (blockIdx.x % hblocks) * MH + (int)threadIdx.x / QPH;
   const int q = threadIdx.x % QPH;
+  if (h >= H) return;
+  const size_t base = ((size_t)s * H + h) * num_parts;
+  // The first kMergeAhead slots of this (sequence, head), and in the grouped
+  // call its first tail slot, are loaded before the lengths that say which of
+  // them hold partials arrive (all lie inside the row; unused ones are
+  // dropped): the lengths' round trip then overlaps the partials'.
+  constexpr int kMergeAhead = 4;
+  float2 aml[kMergeAhead + 1];
+  float4 ao[kMergeAhead + 1];
+#pragma unroll
+  for (int j = 0; j <= kMergeAhead; ++j) {
+    const int slot = j < kMergeAhead ? j : slot_base;
+    if ((j < kMergeAhead || GROUPED) && slot < num_parts) {
+      aml[j] = *reinterpret_cast<const float2*>(ws_ml + (base + slot) * 2);
+      ao[j] = *reinterpret_cast<const float4*>(ws_o + (base + slot) * D + 4 * q);
+    }
+  }
   const int ctx = context_lens[s];
   int n0, n1;
   if constexpr (GROUPED) {
@@ -191,21 +208,17 @@ decode_merge_packed_kernel(uint16_t* __restrict__ out, const float* __restrict__
     const int st = seq_tok0[s];
     n0 = (st + chunk_tokens - 1) / chunk_tokens;
     n1 = (ctx - st + part_tokens - 1) / part_tokens;
+    // keeps the compiler from sinking the length load past the first folds,
+    // which put its round trip at the end
+    asm volatile("" ::"s"(n1));
   } else {
     n0 = (ctx + part_tokens - 1) / part_tokens;
     n1 = 0;
     if (n0 <= 1) return;  // written directly by the partition launch
   }
-  if (h >= H) return;
-  const int n = n0 + n1;
-  const size_t base = ((size_t)s * H + h) * num_parts;
   float M = -INFINITY, L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int i = 0; i < n; ++i) {
-    const size_t pi = base + (i < n0 ? i : slot_base + (i - n0));
-    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + pi * 2);
-    const float4 oi = *reinterpret_cast<const float4*>(ws_o + pi * D + 4 * q);
+  auto fold = [&](const float2 ml, const float4 oi) {
     const float mn = fmaxf(M, ml.x);
     const float a = fast_exp2(M - mn);
     const float w = ml.y * fast_exp2(ml.x - mn);
@@ -215,6 +228,21 @@ decode_merge_packed_kernel(uint16_t* __restrict__ out, const float* __restrict__
     o.z = o.z * a + w * oi.z;
     o.w = o.w * a + w * oi.w;
     M = mn;
+  };
+  // slots 0 .. n0 - 1, then slot_base .. slot_base + n1 - 1, in that order
+#pragma unroll
+  for (int j = 0; j < kMergeAhead; ++j)
+    if (j < n0) fold(aml[j], ao[j]);
+#pragma unroll 4
+  for (int i = kMergeAhead; i < n0; ++i)
+    fold(*reinterpret_cast<const float2*>(ws_ml + (base + i) * 2),
+         *reinterpret_cast<const float4*>(ws_o + (base + i) * D + 4 * q));
+  if constexpr (GROUPED) {
+    if (n1 > 0) fold(aml[kMergeAhead], ao[kMergeAhead]);
+#pragma unroll 4
+    for (int i = 1; i < n1; ++i)
+      fold(*reinterpret_cast<const float2*>(ws_ml + (base + slot_base + i) * 2),
+           *reinterpret_cast<const float4*>(ws_o + (base + slot_base + i) * D + 4 * q));
   }
   const uint2 r = make_uint2(E::pack2(o.x / L, o.y / L), E::pack2(o.z / L, o.w / L));
   *reinterpret_cast<uint2*>(out + ((size_t)s * H + h) * D + 4 * q) = r;
